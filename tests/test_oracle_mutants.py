@@ -1,0 +1,124 @@
+"""The pins catch plausible oracle mistakes.
+
+Each case plants one mistake in a copy of an oracle function (on the CPU only),
+runs the pin tests of tests/test_oracle.py against it, and requires at least
+one of them to fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.h3_oracle as H
+from tests import test_oracle as T
+
+
+def _rms_no_eps(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * gamma
+
+
+def _rms_sum(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _rms_no_gamma(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rope_sign(y, cos, sin):
+    y = np.asarray(y, np.float64)
+    out = np.empty_like(y)
+    out[..., 0::2] = y[..., 0::2] * cos + y[..., 1::2] * sin
+    out[..., 1::2] = -y[..., 0::2] * sin + y[..., 1::2] * cos
+    return out
+
+
+def _rope_half_split(y, cos, sin):
+    y = np.asarray(y, np.float64)
+    h = y.shape[-1] // 2
+    a, b = y[..., :h], y[..., h:]
+    return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)
+
+
+def _tables_wrong_exponent(positions, D=128, theta=10000.0):
+    pos = np.asarray(positions, np.float64)
+    inv = np.power(float(theta), -np.arange(D // 2) / D)
+    ang = pos[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _bf16_double_rounding(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    import torch
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_truncate(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    return (x32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _attn_no_scale(q, k, v, scale, block=256):
+    return H.__dict__["_orig_attention_head"](q, k, v, 1.0, block)
+
+
+def _attn_transposed(q, k, v, scale, block=256):
+    s = scale * (np.asarray(k) @ np.asarray(q).T).T if q.shape[0] == k.shape[0] else scale * (k @ q.T)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e / e.sum(axis=1, keepdims=True)) @ v
+
+
+def _attn_unnormalised(q, k, v, scale, block=256):
+    s = scale * (np.asarray(q) @ np.asarray(k).T)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e @ v
+
+
+def _attn_no_max(q, k, v, scale, block=256):
+    s = scale * (np.asarray(q) @ np.asarray(k).T)
+    with np.errstate(all="ignore"):
+        e = np.exp(s)
+        return (e / e.sum(axis=1, keepdims=True)) @ v
+
+
+def _attn_softmax_over_queries(q, k, v, scale, block=256):
+    s = scale * (np.asarray(q) @ np.asarray(k).T)
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return (e / e.sum(axis=0, keepdims=True)) @ v
+
+
+PIN_TESTS = [getattr(T, n) for n in dir(T) if n.startswith("test_")]
+
+MUTANTS = {
+    "rms_no_eps": ("rms_norm", _rms_no_eps),
+    "rms_sum_not_mean": ("rms_norm", _rms_sum),
+    "rms_no_gamma": ("rms_norm", _rms_no_gamma),
+    "rope_sign": ("rope_rotate", _rope_sign),
+    "rope_half_split": ("rope_rotate", _rope_half_split),
+    "tables_exponent": ("rope_tables", _tables_wrong_exponent),
+    "bf16_double_rounding": ("f64_to_bf16_bits", _bf16_double_rounding),
+    "bf16_truncate": ("f64_to_bf16_bits", _bf16_truncate),
+    "attn_no_scale": ("attention_head", _attn_no_scale),
+    "attn_transposed": ("attention_head", _attn_transposed),
+    "attn_unnormalised": ("attention_head", _attn_unnormalised),
+    "attn_no_max_shift": ("attention_head", _attn_no_max),
+    "attn_softmax_wrong_axis": ("attention_head", _attn_softmax_over_queries),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    fn_name, mutant = MUTANTS[name]
+    monkeypatch.setitem(H.__dict__, "_orig_attention_head", H.attention_head)
+    monkeypatch.setattr(H, fn_name, mutant)
+    monkeypatch.setattr(oracle, fn_name, mutant)
+    failed = []
+    for t in PIN_TESTS:
+        try:
+            t()
+        except Exception:  # an assertion or an error: either way the pin caught it
+            failed.append(t.__name__)
+    assert failed, f"mutant {name} passed every pin"
