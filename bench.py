@@ -1,0 +1,197 @@
+"""Benchmark of one Ulysses rank's H3 attention step on one MI355X.
+
+A step is the whole hot path on one batch: h3_qknorm_rope (q, k in place)
+followed by h3_attention, on seeded synthetic inputs already resident in HBM.
+Default workload: one world_size=8 rank's share, H=7 heads, L=32768 tokens
+(31744 video + 1024 audio), head_dim 128, bf16.
+
+Prints one JSON line: whole-step attention TFLOPS (4*H*L^2*D per step), the
+roofline of the dominant kernel (attention, bf16 MFMA) from HIP events around
+its launches, the prologue's bandwidth, and the oracle's CPU throughput on a
+bounded sample (reported baseline only).
+
+    python bench.py [--steps K] [--warmup W] [--workload ws8] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prologue_bytes(H, L, D=128):
+    """Algorithmic bytes of one prologue launch: q and k read and written
+    (bf16), cos and sin read once, both gamma vectors."""
+    return 8 * H * L * D + 2 * L * (D // 2) * 4 + 2 * D * 4
+
+
+def cpu_baseline(x, w, budget_s=15.0):
+    """The oracle on a bounded sample of the same workload, timed on the host:
+    for heads 0, 1, ... until the budget is spent: the prologue of that head's k
+    (all L rows) and of 512 sampled q rows, then attention for those rows."""
+    import torch
+    import oracle
+    from exact_head_attention_amd import inputs as I
+    cores = torch.get_num_threads()
+    rows_done, heads, t_total = 0, 0, 0.0
+    c_ref, s_ref = oracle.rope_tables(x["positions"], w.D, x["theta"])
+    n_rows = 512
+    for h in range(w.H):
+        rows = I.sample_rows(w, h, n_rows)
+        t0 = time.perf_counter()
+        _, kb = oracle.qknorm_rope(x["k"][h:h + 1], x["gamma_k"], c_ref, s_ref, x["eps"])
+        _, qb = oracle.qknorm_rope(x["q"][h:h + 1, rows], x["gamma_q"], c_ref[rows], s_ref[rows], x["eps"])
+        oracle.attention_head(oracle.bf16_to_f64(qb[0]), oracle.bf16_to_f64(kb[0]),
+                              oracle.bf16_to_f64(x["v"][h]), x["scale"])
+        t_total += time.perf_counter() - t0
+        rows_done += len(rows)
+        heads += 1
+        if t_total >= budget_s:
+            break
+    flops = 4.0 * rows_done * w.L * w.D
+    return {"value": flops / t_total / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} head(s) x {n_rows}+ seeded query rows at L={w.L}: fp64 prologue of the "
+                      f"head's k and the sampled q rows, then exact attention for those rows "
+                      f"({t_total:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ws8")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every rank's share is the same per-GPU kernel with no "
+              "communication inside it, and this build runs on one GPU only (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_head_attention_amd import binding as B
+    from exact_head_attention_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    log(f"bench: workload {w.name} H={w.H} L={w.L} D={w.D}; generating inputs")
+    x = I.make_inputs(w, args.seed)
+    dev = torch.device("cuda:0")
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).view(dt).to(dev)
+
+    q, k, v = (up(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    gq, gk = up(x["gamma_q"], torch.float32), up(x["gamma_k"], torch.float32)
+    pos = up(x["positions"], torch.int32)
+    out = torch.empty_like(q)
+    cos, sin = B.rope_tables(pos, w.D, x["theta"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.qknorm_rope(q, k, gq, gk, cos, sin, x["eps"])
+        if ev is not None:
+            ev[1].record(stream)
+        B.attention(q, k, v, out=out, scale=x["scale"])
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    att_ms_all = [e[1].elapsed_time(e[2]) for e in evs]
+    att_ms = float(np.mean(att_ms_all))
+
+    # Prologue alone with the 256 MB last-level cache flushed before each launch.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    pro_cold = []
+    for _ in range(20):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.qknorm_rope(q, k, gq, gk, cos, sin, x["eps"])
+        b.record(stream)
+        torch.cuda.synchronize()
+        pro_cold.append(a.elapsed_time(b))
+    del flush
+    pro_cold_ms = float(np.median(pro_cold))
+
+    flops = w.flops
+    value = flops / (ms_step / 1e3) / 1e12
+    att_tflops = flops / (att_ms / 1e3) / 1e12
+    pbytes = prologue_bytes(w.H, w.L, w.D)
+    rec = {
+        "metric": "attention TFLOPS (4*H*L^2*D per step, prologue included) and % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, gamma 1+0.1N(0,1); packed video+audio RoPE positions)",
+        "config": {"workload": f"{w.name}: one Ulysses rank's share, H={w.H} heads, L={w.L} "
+                               f"({w.n_video} video + {w.n_audio} audio tokens), D={w.D}",
+                   "H": w.H, "L": w.L, "D": w.D, "seed": args.seed},
+        "pct_of_bf16_peak": round(100 * value / BF16_MFMA_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": "attn_fwd_kernel", "bound": "mfma", "achieved": round(att_tflops, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(att_ms, 4), "min_launch_ms": round(min(att_ms_all), 4),
+                     "flops_per_launch": flops},
+        "prologue": {"kernel": "qknorm_rope_kernel", "bound": "hbm",
+                     "avg_launch_us_in_step": round(pro_ms * 1e3, 2),
+                     "cold_median_us": round(pro_cold_ms * 1e3, 2),
+                     "achieved_GBps_cold": round(pbytes / (pro_cold_ms / 1e3) / 1e9, 1),
+                     "peak_GBps": HBM_PEAK_GBS,
+                     "frac_cold": round(pbytes / (pro_cold_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": pbytes},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

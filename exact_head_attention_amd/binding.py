@@ -1,0 +1,116 @@
+"""Python binding of libh3attn.so (ctypes).  Argument marshalling only.
+
+Tensors are PyTorch device tensors on the current HIP device; every call is
+enqueued on torch's current stream.  The binding checks dtypes, shapes and
+contiguity, passes raw pointers, and raises H3Error on a nonzero status.  There
+is no fallback: if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m exact_head_attention_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _f, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+lib.h3_qknorm_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _f, _vp]
+lib.h3_qknorm_rope.restype = _i
+lib.h3_attention.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _f, _vp]
+lib.h3_attention.restype = _i
+lib.h3_rope_tables.argtypes = [_vp, _i, _i, _d, _vp, _vp, _vp]
+lib.h3_rope_tables.restype = _i
+lib.h3_status_string.argtypes = [_i]
+lib.h3_status_string.restype = ctypes.c_char_p
+lib.h3_abi_version.argtypes = []
+lib.h3_abi_version.restype = _i
+
+HEAD_DIM = 128
+EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_status_string", "h3_abi_version")
+
+
+class H3Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib.h3_status_string(status).decode()} (status {status})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise H3Error(fn, status)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _hld(t, name):
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [H, L, {HEAD_DIM}], got {tuple(t.shape)}")
+    return t.shape[0], t.shape[1], t.shape[2]
+
+
+def rope_tables(positions, D: int = HEAD_DIM, theta: float = 10000.0):
+    """cos, sin fp32 [L, D/2] of positions (int32 [L], on the GPU)."""
+    import torch
+    L = positions.shape[0]
+    cos = torch.empty((L, D // 2), dtype=torch.float32, device=positions.device)
+    sin = torch.empty_like(cos)
+    _check("h3_rope_tables", lib.h3_rope_tables(_dev(positions, torch.int32, "positions"), L, D,
+                                                float(theta), _dev(cos, torch.float32, "cos"),
+                                                _dev(sin, torch.float32, "sin"), _stream()))
+    return cos, sin
+
+
+def qknorm_rope(q, k, gamma_q, gamma_k, cos, sin, eps: float = 1e-6) -> None:
+    """In place: q, k (bf16 [H, L, 128]) <- RoPE(RMSNorm(x) * gamma)."""
+    import torch
+    H, L, D = _hld(q, "q")
+    if tuple(k.shape) != (H, L, D):
+        raise ValueError("k must have q's shape")
+    if tuple(cos.shape) != (L, D // 2) or tuple(sin.shape) != (L, D // 2):
+        raise ValueError(f"cos/sin must be [{L}, {D // 2}]")
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError(f"gamma_q/gamma_k must have {D} elements")
+    _check("h3_qknorm_rope", lib.h3_qknorm_rope(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+        _dev(gamma_q, torch.float32, "gamma_q"), _dev(gamma_k, torch.float32, "gamma_k"),
+        _dev(cos, torch.float32, "cos"), _dev(sin, torch.float32, "sin"),
+        H, L, D, float(eps), _stream()))
+
+
+def attention(q, k, v, out=None, scale: float | None = None):
+    """out = softmax(scale q k^T) v per head; bf16 [H, L, 128].  Returns out."""
+    import torch
+    H, L, D = _hld(q, "q")
+    if tuple(k.shape) != (H, L, D) or tuple(v.shape) != (H, L, D):
+        raise ValueError("k and v must have q's shape")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != (H, L, D):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("h3_attention", lib.h3_attention(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(out, torch.bfloat16, "out"), H, L, D, float(scale), _stream()))
+    return out

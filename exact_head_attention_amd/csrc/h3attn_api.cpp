@@ -1,0 +1,110 @@
+// Host side of the C ABI in include/h3attn.h: argument validation, then one
+// launch on the caller's stream.  Validation runs before any HIP call, so the
+// error paths need no GPU.
+#include "h3attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "h3attn_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// H*L*D elements must be addressable with 64-bit offsets and the row count
+// must stay below 2^31 (grid and row indices are 32-bit).
+bool shape_ok(int H, int L) {
+  if (H < 1 || L < 1) return false;
+  const int64_t rows = static_cast<int64_t>(H) * L;
+  return rows < (int64_t{1} << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3_abi_version(void) { return H3ATTN_ABI_VERSION; }
+
+const char *h3_status_string(int status) {
+  switch (status) {
+    case H3_OK: return "ok";
+    case H3_ERR_NULL: return "a required pointer is NULL";
+    case H3_ERR_SHAPE: return "H and L must be >= 1 and H*L < 2^31";
+    case H3_ERR_UNSUPPORTED: return "only head_dim D == 128 is supported";
+    case H3_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
+    case H3_ERR_ALIAS: return "output and input buffers overlap";
+    case H3_ERR_VALUE: return "eps, scale or theta is out of range or not finite";
+    case H3_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    default: return "unknown h3attn status";
+  }
+}
+
+int h3_qknorm_rope(void *q, void *k, const float *gamma_q, const float *gamma_k,
+                   const float *cos, const float *sin, int H, int L, int D,
+                   float eps, void *stream) {
+  if (!q || !k || !gamma_q || !gamma_k || !cos || !sin) return H3_ERR_NULL;
+  if (!shape_ok(H, L)) return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(gamma_q) || !aligned16(gamma_k) ||
+      !aligned16(cos) || !aligned16(sin))
+    return H3_ERR_ALIGN;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return H3_ERR_VALUE;
+  const uint64_t tensor_bytes = static_cast<uint64_t>(H) * L * D * 2;
+  const uint64_t table_bytes = static_cast<uint64_t>(L) * (D / 2) * 4;
+  if (overlaps(q, tensor_bytes, k, tensor_bytes)) return H3_ERR_ALIAS;
+  if (overlaps(cos, table_bytes, q, tensor_bytes) || overlaps(cos, table_bytes, k, tensor_bytes) ||
+      overlaps(sin, table_bytes, q, tensor_bytes) || overlaps(sin, table_bytes, k, tensor_bytes) ||
+      overlaps(gamma_q, D * 4u, q, tensor_bytes) || overlaps(gamma_q, D * 4u, k, tensor_bytes) ||
+      overlaps(gamma_k, D * 4u, q, tensor_bytes) || overlaps(gamma_k, D * 4u, k, tensor_bytes))
+    return H3_ERR_ALIAS;
+  hipError_t e = h3::launch_qknorm_rope(static_cast<uint16_t *>(q), static_cast<uint16_t *>(k),
+                                        gamma_q, gamma_k, cos, sin, H, L, eps,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_attention(const void *q, const void *k, const void *v, void *out,
+                 int H, int L, int D, float scale, void *stream) {
+  if (!q || !k || !v || !out) return H3_ERR_NULL;
+  if (!shape_ok(H, L)) return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return H3_ERR_ALIGN;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return H3_ERR_ALIAS;
+  if (h3::attention_grid(H, L) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
+  hipError_t e = h3::launch_attention(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                      static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out),
+                                      H, L, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_rope_tables(const int *positions, int L, int D, double theta,
+                   float *cos, float *sin, void *stream) {
+  if (!positions || !cos || !sin) return H3_ERR_NULL;
+  if (L < 1) return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(positions) & 3u) != 0 || !aligned16(cos) || !aligned16(sin))
+    return H3_ERR_ALIGN;
+  if (!(theta > 1.0) || !std::isfinite(theta)) return H3_ERR_VALUE;
+  const uint64_t table_bytes = static_cast<uint64_t>(L) * (D / 2) * 4;
+  if (overlaps(cos, table_bytes, sin, table_bytes) ||
+      overlaps(positions, static_cast<uint64_t>(L) * 4, cos, table_bytes) ||
+      overlaps(positions, static_cast<uint64_t>(L) * 4, sin, table_bytes))
+    return H3_ERR_ALIAS;
+  if (static_cast<int64_t>(L) * (D / 2) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
+  hipError_t e = h3::launch_rope_tables(positions, L, D / 2, theta, cos, sin,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// Launchers shared between the host API (h3attn_api.cpp) and the kernels.
+// Arguments reaching these have already been validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+constexpr int kHeadDim = 128;
+
+hipError_t launch_qknorm_rope(uint16_t *q, uint16_t *k, const float *gamma_q,
+                              const float *gamma_k, const float *cos_t,
+                              const float *sin_t, int H, int L, float eps,
+                              hipStream_t stream);
+
+hipError_t launch_rope_tables(const int *positions, int L, int half,
+                              double theta, float *cos_t, float *sin_t,
+                              hipStream_t stream);
+
+// Number of workgroups h3_attention launches for H heads of L tokens.
+int64_t attention_grid(int H, int L);
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, uint16_t *out, int H, int L,
+                            float scale, hipStream_t stream);
+
+}  // namespace h3

@@ -1,0 +1,146 @@
+// QK-RMSNorm + RoPE prologue and the rotary-table builder, for gfx950.
+//
+// The prologue is a streaming, HBM-bound kernel: every q and k row (128 bf16 =
+// 256 B) is read once and written once, in place.  One 16-lane row of a wave
+// owns one token: each lane holds 8 consecutive elements (one 16-byte load),
+// i.e. four adjacent RoPE pairs, so the pair rotation is lane-local and only
+// the sum of squares crosses lanes (a 16-lane DPP reduction).  The token's cos
+// and sin (64 fp32 each, shared by every head) are loaded once and reused for
+// all H heads of q and of k, so the tables cross HBM once per token.
+//
+// Math follows "Tensor parallelism for MiniMax-H3", PR description (head_dim-
+// shaped QK-norm after the head split; real cos/sin broadcast over heads):
+// fp32 throughout, one round-to-nearest-even to bf16 at the store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3attn_internal.h"
+
+namespace h3 {
+namespace {
+
+constexpr int kTokensPerBlock = 16;   // 256 threads = 16 rows of 16 lanes
+constexpr int kHeadUnroll = 4;        // heads whose loads are in flight together
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even) and pack them, lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Sum over the 16 lanes of a DPP row; every lane gets the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  return v;
+}
+
+// Normalise, scale by gamma and rotate one lane's 8 elements (4 pairs).
+__device__ __forceinline__ uint4 norm_rope8(uint4 raw, const float g[8], const float c[4],
+                                            const float s[4], float eps) {
+  float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+  ss = row16_sum(ss);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + eps);
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float y0 = x[2 * p] * r * g[2 * p];
+    const float y1 = x[2 * p + 1] * r * g[2 * p + 1];
+    const float o0 = y0 * c[p] - y1 * s[p];
+    const float o1 = y0 * s[p] + y1 * c[p];
+    w[p] = pack_bf16x2(o0, o1);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(
+    uint16_t *__restrict__ q, uint16_t *__restrict__ k, const float *__restrict__ gamma_q,
+    const float *__restrict__ gamma_k, const float *__restrict__ cos_t,
+    const float *__restrict__ sin_t, int H, int L, float eps) {
+  const int sub = threadIdx.x & 15;                       // lane within the 16-lane row
+  const int tok = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 4);
+  if (tok >= L) return;                                   // whole 16-lane rows exit together
+
+  const float4 c4 = *reinterpret_cast<const float4 *>(cos_t + static_cast<size_t>(tok) * 64 + 4 * sub);
+  const float4 s4 = *reinterpret_cast<const float4 *>(sin_t + static_cast<size_t>(tok) * 64 + 4 * sub);
+  const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+  const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+  float gq[8], gk[8];
+  {
+    const float4 a = *reinterpret_cast<const float4 *>(gamma_q + 8 * sub);
+    const float4 b = *reinterpret_cast<const float4 *>(gamma_q + 8 * sub + 4);
+    const float4 e = *reinterpret_cast<const float4 *>(gamma_k + 8 * sub);
+    const float4 f = *reinterpret_cast<const float4 *>(gamma_k + 8 * sub + 4);
+    gq[0] = a.x; gq[1] = a.y; gq[2] = a.z; gq[3] = a.w; gq[4] = b.x; gq[5] = b.y; gq[6] = b.z; gq[7] = b.w;
+    gk[0] = e.x; gk[1] = e.y; gk[2] = e.z; gk[3] = e.w; gk[4] = f.x; gk[5] = f.y; gk[6] = f.z; gk[7] = f.w;
+  }
+
+  const size_t head_stride = static_cast<size_t>(L) * kHeadDim;
+  const size_t row_off = static_cast<size_t>(tok) * kHeadDim + 8 * sub;
+  for (int h0 = 0; h0 < H; h0 += kHeadUnroll) {
+    uint4 rq[kHeadUnroll], rk[kHeadUnroll];
+#pragma unroll
+    for (int u = 0; u < kHeadUnroll; ++u) {
+      if (h0 + u < H) {
+        rq[u] = *reinterpret_cast<const uint4 *>(q + (h0 + u) * head_stride + row_off);
+        rk[u] = *reinterpret_cast<const uint4 *>(k + (h0 + u) * head_stride + row_off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kHeadUnroll; ++u) {
+      if (h0 + u < H) {
+        *reinterpret_cast<uint4 *>(q + (h0 + u) * head_stride + row_off) = norm_rope8(rq[u], gq, c, s, eps);
+        *reinterpret_cast<uint4 *>(k + (h0 + u) * head_stride + row_off) = norm_rope8(rk[u], gk, c, s, eps);
+      }
+    }
+  }
+}
+
+// cos/sin of positions[i] * theta^(-2j/D) in fp64, rounded once to fp32.
+__global__ __launch_bounds__(256) void rope_tables_kernel(const int *__restrict__ positions, int L, int half,
+                                                          double theta, float *__restrict__ cos_t,
+                                                          float *__restrict__ sin_t) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= L * half) return;
+  const int i = idx / half;
+  const int j = idx - i * half;
+  const double inv_freq = pow(theta, (-2.0 * j) / (2 * half));
+  const double angle = static_cast<double>(positions[i]) * inv_freq;
+  double sn, cs;
+  sincos(angle, &sn, &cs);
+  cos_t[idx] = static_cast<float>(cs);
+  sin_t[idx] = static_cast<float>(sn);
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(uint16_t *q, uint16_t *k, const float *gamma_q, const float *gamma_k,
+                              const float *cos_t, const float *sin_t, int H, int L, float eps,
+                              hipStream_t stream) {
+  const int blocks = (L + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(blocks), dim3(256), 0, stream, q, k, gamma_q, gamma_k,
+                     cos_t, sin_t, H, L, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tables(const int *positions, int L, int half, double theta, float *cos_t,
+                              float *sin_t, hipStream_t stream) {
+  const int n = L * half;
+  hipLaunchKernelGGL(rope_tables_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, positions, L, half,
+                     theta, cos_t, sin_t);
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,123 @@
+/*
+ * h3attn.h -- C ABI of the MI355X (gfx950) library for one Ulysses rank's
+ * exact attention in MiniMax-H3, with its QK-RMSNorm + RoPE prologue.
+ *
+ * Where the operations come from:
+ *   - "buqi-minimax-h3-multigpu" (README), How it works: every rank computes
+ *     exact full attention over the full packed sequence for 56/world_size
+ *     heads; On accuracy: nothing is approximated, masked or cached.
+ *   - "Tensor parallelism for MiniMax-H3" (diffusers PR), PR description:
+ *     QK-norms are head_dim-shaped and applied after the head split; the
+ *     rotary embedding uses real sin/cos that broadcast over the head axis.
+ *     whn09's comment (Bug: non-persistent buffers): rotary angles come from
+ *     inv_freq and position ids.  whn09's Neuron FYI: the attention is packed
+ *     full self-attention with no mask, and the real sequence length need not
+ *     be a multiple of any tile size.
+ *
+ * Conventions for every call:
+ *   - Tensors are row-major with batch 1: q, k, v, out are bf16 [H][L][D]
+ *     (element (h, i, d) at offset (h*L + i)*D + d).  D must be 128 (MiniMax-
+ *     H3's head_dim: inner width 7168 over 56 heads).
+ *   - Pointers are device pointers on the current HIP device, owned by the
+ *     caller.  The library allocates nothing and keeps no mutable state, so
+ *     calls are thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; a return of H3_OK means "validated and launched".  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Arguments are validated before anything is launched.  On error the call
+ *     returns a negative h3_status, launches nothing, writes nothing and
+ *     prints nothing.
+ *   - Head splits: heads are independent, so a caller may pass pointers offset
+ *     by h0*L*D with a smaller H.  Per-head results are bit-identical for any
+ *     split and across repeated calls.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3ATTN_ABI_VERSION 1
+#define H3ATTN_HEAD_DIM 128
+
+typedef enum {
+  H3_OK = 0,
+  H3_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  H3_ERR_SHAPE = -2,       /* H < 1, L < 1, or a size/grid that overflows         */
+  H3_ERR_UNSUPPORTED = -3, /* D != 128                                            */
+  H3_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned             */
+  H3_ERR_ALIAS = -5,       /* out overlaps q, k or v; q overlaps k; cos overlaps sin */
+  H3_ERR_VALUE = -6,       /* eps <= 0 or not finite; scale <= 0 or not finite;   */
+                           /* theta <= 1 or not finite                            */
+  H3_ERR_LAUNCH = -7       /* the HIP runtime refused the launch                  */
+} h3_status;
+
+/*
+ * QK-RMSNorm followed by RoPE, applied to q and to k in place.
+ *
+ * For every head h and token i, with x = q[h][i][:] (gamma = gamma_q) and
+ * again with x = k[h][i][:] (gamma = gamma_k):
+ *   r     = 1 / sqrt(mean_d(x_d^2) + eps)
+ *   y_d   = x_d * r * gamma_d
+ *   x'_2j   = y_2j * cos[i][j] - y_2j+1 * sin[i][j]      j = 0 .. D/2-1
+ *   x'_2j+1 = y_2j * sin[i][j] + y_2j+1 * cos[i][j]
+ * computed in fp32 and rounded once to bf16 (round to nearest even), written
+ * back over x.  The norm is the head_dim-shaped QK-norm after the head split;
+ * the tables broadcast over heads (see the passages above).
+ *
+ *   q, k          bf16 [H][L][D], read and overwritten.  Must not overlap.
+ *   gamma_q/_k    fp32 [D], shared by all heads.
+ *   cos, sin      fp32 [L][D/2]: entry (i, j) is cos/sin of token i's rotary
+ *                 angle for pair j (h3_rope_tables builds them).
+ *   H, L, D       heads, tokens, head_dim (== 128).
+ *   eps           > 0, added to the mean of squares inside the square root.
+ * All pointers must be 16-byte aligned.
+ */
+int h3_qknorm_rope(void *q, void *k, const float *gamma_q, const float *gamma_k,
+                   const float *cos, const float *sin, int H, int L, int D,
+                   float eps, void *stream);
+
+/*
+ * Exact, unmasked, non-causal attention per head:
+ *   out[h][i][:] = sum_j softmax_j(scale * <q[h][i], k[h][j]>) * v[h][j][:]
+ * over all L keys of head h.  bf16 inputs, bf16 MFMA products with fp32
+ * accumulation, online softmax in fp32, output rounded once to bf16.  Any
+ * L >= 1 is accepted; a partial last tile is predicated, never padded.
+ *
+ *   q, k, v       bf16 [H][L][D], read only.
+ *   out           bf16 [H][L][D], written; must not overlap q, k or v.
+ *   scale         > 0 and finite (MiniMax-H3 uses 1/sqrt(128)).
+ * All tensor pointers must be 16-byte aligned.
+ */
+int h3_attention(const void *q, const void *k, const void *v, void *out,
+                 int H, int L, int D, float scale, void *stream);
+
+/*
+ * Rotary tables for h3_qknorm_rope:
+ *   inv_freq_j = theta^(-2j/D),  angle = positions[i] * inv_freq_j,
+ *   cos[i][j] = cos(angle), sin[i][j] = sin(angle),   j = 0 .. D/2-1,
+ * computed in fp64 and rounded once to fp32.  The angle is position times
+ * inv_freq ("Tensor parallelism for MiniMax-H3", whn09's comment on the
+ * rotary inv_freq buffer); theta = 10000 for MiniMax-H3's synthetic layout.
+ *
+ *   positions     int32 [L], device memory: the rotary position of each
+ *                 packed token (e.g. video 0..Lv-1 then audio restarting at 0).
+ *   cos, sin      fp32 [L][D/2], written; must not overlap.
+ *   theta         > 1 and finite.
+ * cos and sin must be 16-byte aligned; positions 4-byte aligned.
+ */
+int h3_rope_tables(const int *positions, int L, int D, double theta,
+                   float *cos, float *sin, void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *h3_status_string(int status);
+
+/* H3ATTN_ABI_VERSION of the built library. */
+int h3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

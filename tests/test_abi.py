@@ -1,0 +1,100 @@
+"""The C ABI library loads, exports what include/h3attn.h declares, and rejects
+invalid arguments before touching the GPU (no compute call needs a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from exact_head_attention_amd import binding
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_status_string", "h3_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    for name in _declared_functions():
+        assert hasattr(B.lib, name), name
+    assert B.lib.h3_abi_version() == 1
+
+
+def test_status_strings(B):
+    for code in range(0, -8, -1):
+        s = B.lib.h3_status_string(code)
+        assert s and len(s) >= 2
+    assert b"unknown" in B.lib.h3_status_string(42)
+
+
+# Fake, never-dereferenced device addresses: validation rejects these calls
+# before any HIP call is made.
+A = 0x7F0000000000
+MB = 1 << 20
+
+
+def _attn(B, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, H=2, L=512, D=128, scale=0.088):
+    return B.lib.h3_attention(q, k, v, o, H, L, D, scale, None)
+
+
+def _pro(B, q=A, k=A + 64 * MB, gq=A + 128 * MB, gk=A + 129 * MB, c=A + 130 * MB, s=A + 140 * MB,
+         H=2, L=512, D=128, eps=1e-6):
+    return B.lib.h3_qknorm_rope(q, k, gq, gk, c, s, H, L, D, eps, None)
+
+
+def _tab(B, p=A, L=512, D=128, theta=10000.0, c=A + 1 * MB, s=A + 2 * MB):
+    return B.lib.h3_rope_tables(p, L, D, theta, c, s, None)
+
+
+def test_attention_argument_errors(B):
+    assert _attn(B, q=None) == -1 and _attn(B, o=None) == -1
+    assert _attn(B, H=0) == -2 and _attn(B, L=0) == -2 and _attn(B, L=-5) == -2
+    assert _attn(B, H=1 << 16, L=1 << 16) == -2
+    assert _attn(B, D=64) == -3 and _attn(B, D=129) == -3
+    assert _attn(B, q=A + 8) == -4 and _attn(B, o=A + 192 * MB + 2) == -4
+    assert _attn(B, o=A + 64 * MB + 16) == -5              # out overlaps k
+    assert _attn(B, o=A) == -5                             # out is q
+    assert _attn(B, scale=0.0) == -6 and _attn(B, scale=-1.0) == -6
+    assert _attn(B, scale=float("inf")) == -6 and _attn(B, scale=float("nan")) == -6
+
+
+def test_prologue_argument_errors(B):
+    assert _pro(B, q=None) == -1 and _pro(B, s=None) == -1 and _pro(B, gk=None) == -1
+    assert _pro(B, H=0) == -2 and _pro(B, L=0) == -2
+    assert _pro(B, D=256) == -3
+    assert _pro(B, c=A + 130 * MB + 4) == -4 and _pro(B, k=A + 64 * MB + 2) == -4
+    assert _pro(B, k=A) == -5                               # q and k are one buffer
+    assert _pro(B, c=A + 16) == -5                          # cos inside q
+    assert _pro(B, eps=0.0) == -6 and _pro(B, eps=float("nan")) == -6 and _pro(B, eps=-1e-6) == -6
+
+
+def test_rope_table_argument_errors(B):
+    assert _tab(B, p=None) == -1 and _tab(B, c=None) == -1
+    assert _tab(B, L=0) == -2
+    assert _tab(B, D=96) == -3
+    assert _tab(B, p=A + 2) == -4 and _tab(B, s=A + 2 * MB + 4) == -4
+    assert _tab(B, s=A + 1 * MB + 64) == -5
+    assert _tab(B, theta=1.0) == -6 and _tab(B, theta=float("inf")) == -6
+
+
+def test_binding_rejects_cpu_tensors(B):
+    import torch
+    q = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        B.attention(q, q, q)
+    with pytest.raises(ValueError):
+        B.attention(torch.zeros(1, 4, 64, dtype=torch.bfloat16), q, q)
