@@ -36,7 +36,11 @@ namespace h3 {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = kHeadDim;
 constexpr int kWaves = 8;
@@ -44,27 +48,35 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBr = kWaves * 32;     // query rows per workgroup
 constexpr int kBc = 64;              // keys per tile
 constexpr int kKStride = D + 8;      // bf16 per K row in LDS (272 B: rows shift 4 banks)
-constexpr int kVStride = kBc + 8;    // bf16 per V^T row in LDS (144 B)
+constexpr int kVStride = D + 32;     // bf16 per V row in LDS (320 B: transpose reads hit 4 disjoint bank windows)
 constexpr float kLog2e = 1.4426950408889634f;
+// The running max is raised only when a tile's max exceeds it by more than
+// kTau (base-2 units), so unnormalised weights stay <= 2^kTau = 256 (exact in
+// bf16's range; fp32 sums).  Any offset cancels between numerator and
+// denominator, so this changes rounding only, never the result's definition.
+constexpr float kTau = 8.0f;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data, gfx9 encoding
 
 __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// Two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32; lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &s, int base) {
-  uint4 w;
-  w.x = pack_bf16x2(s[base + 0], s[base + 1]);
-  w.y = pack_bf16x2(s[base + 2], s[base + 3]);
-  w.z = pack_bf16x2(s[base + 4], s[base + 5]);
-  w.w = pack_bf16x2(s[base + 6], s[base + 7]);
-  return __builtin_bit_cast(bf16x8, w);
+// Buffer loads: the hardware returns zeros past num_records bytes, so ragged
+// tails need no branches and never touch memory outside the head.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
+}
+__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // Maps the hardware's round-robin placement of blocks over the 8 XCDs onto
@@ -76,11 +88,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
 }
 
+__device__ __forceinline__ float lane_half_max(float x) {
+  // Lanes l and l^32 hold the same query row's two key halves.
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __builtin_fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, int L, int n_qtiles, float scale_log2e) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBc * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBc * kVStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -93,152 +115,213 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const uint16_t *Qh = Q + head_off;
   const uint16_t *Kh = K + head_off;
   const uint16_t *Vh = V + head_off;
+  const int row_bytes = D * 2;
 
   // Q^T fragments (B operand): lane holds query row qrow, d = 16c + 8g .. +7.
   const int qrow = qt * kBr + wave * 32 + l32;
-  const bool qvalid = qrow < L;
   bf16x8 qf[8];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, L * row_bytes);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (qvalid) w = *reinterpret_cast<const uint4 *>(Qh + static_cast<size_t>(qrow) * D + 16 * c + 8 * g);
-    qf[c] = __builtin_bit_cast(bf16x8, w);
+    for (int c = 0; c < 8; ++c)
+      qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, qrow * row_bytes + 32 * c + 16 * g));
   }
+
+  // Staging of one key tile: 64 rows x 16 chunks of 16 B for each of K and
+  // V; thread takes chunks tid and tid + 512 (tile-relative byte offset
+  // chunk * 16).  Both land row-major in LDS.
+  auto load_kv = [&](const uint16_t *base, int kt, uint4 (&r)[2]) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (L - kt * kBc) * row_bytes);
+    r[0] = bload128(rs, tid * 16);
+    r[1] = bload128(rs, (tid + kThreads) * 16);
+  };
+  auto store_rows = [&](uint16_t *dst, int stride, const uint4 (&r)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4 *>(dst + (c >> 4) * stride + (c & 15) * 8) = r[i];
+    }
+  };
+
+  // S^T = K_tile . Q^T for the tile in k_lds[buf]; two independent chains.
+  const int krow = swap_bits23(l32);
+  auto compute_s = [&](int buf, f32x16 (&s)[2]) {
+    const uint16_t *kp0 = &k_lds[buf][krow * kKStride + 8 * g];
+    const uint16_t *kp1 = kp0 + 32 * kKStride;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0 + 16 * c);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kp1 + 16 * c);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[1], 0, 0, 0);
+    }
+  };
 
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -__builtin_inff();  // running max, base-2 scaled units
-  float l_run = 0.f;                // this lane's partial row sum
+  float l_run0 = 0.f, l_run1 = 0.f; // this lane's partial row sums of the bf16 weights
 
-  // Global -> register staging of one key tile.
-  //   K: 64 rows x 16 chunks of 16 B; thread takes chunks tid and tid + 512.
-  //   V: thread takes d pair (2*vd, 2*vd+1) of keys 8*vk .. 8*vk+7 (4 B each),
-  //      so every 64-lane load covers one whole 256-byte V row.
-  const int vd = tid & 63, vk = tid >> 6;
-  uint4 kreg[2];
-  uint32_t vreg[8];
   const int n_kt = (L + kBc - 1) / kBc;
-
-  auto gload = [&](int kt) {
-    const int key0 = kt * kBc;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = key0 + (c >> 4);
-      kreg[i] = key < L ? *reinterpret_cast<const uint4 *>(Kh + static_cast<size_t>(key) * D + (c & 15) * 8)
-                        : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = key0 + 8 * vk + j;
-      vreg[j] = key < L ? *reinterpret_cast<const uint32_t *>(Vh + static_cast<size_t>(key) * D + 2 * vd) : 0u;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[i];
-    }
-    uint4 lo, hi;
-    lo.x = (vreg[0] & 0xffffu) | (vreg[1] << 16);
-    lo.y = (vreg[2] & 0xffffu) | (vreg[3] << 16);
-    lo.z = (vreg[4] & 0xffffu) | (vreg[5] << 16);
-    lo.w = (vreg[6] & 0xffffu) | (vreg[7] << 16);
-    hi.x = (vreg[0] >> 16) | (vreg[1] & 0xffff0000u);
-    hi.y = (vreg[2] >> 16) | (vreg[3] & 0xffff0000u);
-    hi.z = (vreg[4] >> 16) | (vreg[5] & 0xffff0000u);
-    hi.w = (vreg[6] >> 16) | (vreg[7] & 0xffff0000u);
-    *reinterpret_cast<uint4 *>(&vt_lds[buf][(2 * vd) * kVStride + 8 * vk]) = lo;
-    *reinterpret_cast<uint4 *>(&vt_lds[buf][(2 * vd + 1) * kVStride + 8 * vk]) = hi;
-  };
-
-  gload(0);
-  lstore(0);
+  // Staging registers, two sets: a step stores the set loaded one step
+  // earlier and refills the other, so global-load latency hides behind a
+  // whole step.  Set layout: [0..1] K chunks, [2..3] V chunks.
+  uint4 stage0[4], stage1[4];
+  {
+    uint4 k0[2], v0[2], k1[2];
+    load_kv(Kh, 0, k0);
+    load_kv(Vh, 0, v0);
+    load_kv(Kh, 1, k1);
+    load_kv(Kh, 2, *reinterpret_cast<uint4(*)[2]>(&stage0[0]));
+    load_kv(Vh, 1, *reinterpret_cast<uint4(*)[2]>(&stage0[2]));
+    store_rows(k_lds[0], kKStride, k0);
+    store_rows(v_lds[0], kVStride, v0);
+    store_rows(k_lds[1], kKStride, k1);
+  }
   __syncthreads();
 
-  const int krow = swap_bits23(l32);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) gload(kt + 1);
+  const uint16_t *kfrag = &k_lds[0][swap_bits23(l32) * kKStride + 8 * g];
+  // Transposed V reads: within each 16-lane group, lane L names row
+  // 8g + L/4 (+4 for the second read) and columns 16*dhalf + 4*(L%4) .. +3;
+  // the hardware hands lane j of the group column 16*dhalf + j of the four
+  // named rows, i.e. V[8g + 0..7][32db + l32] across the two reads.
+  const uint16_t *vfrag = &v_lds[0][(8 * g + ((lane & 15) >> 2)) * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
+  auto vread = [&](const uint16_t *src) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * kVStride));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto kread = [&](const uint16_t *kp, int b, int c) {
+    return *reinterpret_cast<const bf16x8 *>(kp + b * 32 * kKStride + 16 * c);
+  };
 
-    // S^T = K_tile . Q^T for the two 32-key blocks.
-    f32x16 s[2];
+  f32x16 s_a[2], s_b[2];
+  {
+    s_a[0] = f32x16{};
+    s_a[1] = f32x16{};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-      const uint16_t *kp = &k_lds[buf][(32 * b + krow) * kKStride + 8 * g];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 16 * c);
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[b], 0, 0, 0);
-      }
+    for (int c = 0; c < 8; ++c) {
+      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kfrag, 0, c), qf[c], s_a[0], 0, 0, 0);
+      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kfrag, 1, c), qf[c], s_a[1], 0, 0, 0);
     }
+  }
 
-    // Accumulator s[b][i] holds key kt*64 + 32b + 16(i/8) + 8g + i%8.
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  // One key tile: softmax of s_cur (tile kt), scores of tile kt+1 into s_nxt,
+  // O += P.V for tile kt, then LDS staging of K tile kt+2 and V tile kt+1
+  // from st_store while st_load fetches K tile kt+3 and V tile kt+2.
+  auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 (&st_store)[4], uint4 (&st_load)[4]) {
+    // (1) Mask the ragged tail, row max, and (rarely) raise the running max.
+    // s_cur[b][i] holds key kt*64 + 32b + 16(i/8) + 8g + i%8.
     const int key_base = kt * kBc;
     if (key_base + kBc > L) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= L) s[b][i] = -__builtin_inff();
+          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= L) s_cur[b][i] = -__builtin_inff();
     }
+    float mx = s_cur[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(mx, s_cur[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s_cur[1][i]);
+    const float mxs = lane_half_max(mx) * scale_log2e;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0) {
+      const float m_new = __builtin_fmaxf(m_run, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run0 *= alpha;
+      l_run1 *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float neg_m = -m_run;
 
-    float mx = s[0][0];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[b][i]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx * scale_log2e);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    load_kv(Kh, kt + 3, *reinterpret_cast<uint4(*)[2]>(&st_load[0]));
+    load_kv(Vh, kt + 2, *reinterpret_cast<uint4(*)[2]>(&st_load[2]));
 
-    float psum = 0.f;
+    // (2) Scores of tile kt+1 on the matrix cores, interleaved step by step
+    // with the exponentials of tile kt on the vector ALUs; K fragments are
+    // read one step ahead.
+    const uint16_t *kp = kfrag + ((kt + 1) & 1) * (kBc * kKStride);
+    uint32_t pw[16];
+    bf16x8 a0 = kread(kp, 0, 0), a1 = kread(kp, 1, 0);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][i], scale_log2e, -m_new));
-        s[b][i] = p;
-        psum += p;
+    for (int c = 0; c < 8; ++c) {
+      bf16x8 n0 = a0, n1 = a1;
+      if (c < 7) {
+        n0 = kread(kp, 0, c + 1);
+        n1 = kread(kp, 1, c + 1);
       }
-    l_run = __builtin_fmaf(l_run, alpha, psum);
+      s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      pf[b][0] = to_bf16x8(s[b], 0);
-      pf[b][1] = to_bf16x8(s[b], 8);
+      for (int e = 0; e < 2; ++e) {
+        const int b = c >> 2, i = 4 * (c & 3) + 2 * e;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i], scale_log2e, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i + 1], scale_log2e, neg_m));
+        pw[2 * c + e] = pack_bf16x2(p0, p1);
+        if (e == 0)
+          l_run0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run0, false);
+        else
+          l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run1, false);
+      }
+      s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
+      if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next step's 2 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
     }
 
-    // O^T += V_tile^T . P^T
+    // (3) O^T += V_tile^T . P^T.  pw[4*(2b+t) + 0..3] holds the bf16 weights
+    // of keys 32b + 16t + 8g + 0..7, the same keys the transposed V reads
+    // deliver for k-step bt = 2b + t.  V fragments are read one k-step ahead.
+    const uint16_t *vp = vfrag + (kt & 1) * (kBc * kVStride);
+    bf16x8 vf[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint16_t *vp = &vt_lds[buf][(32 * db + l32) * kVStride + 8 * g];
+    for (int db = 0; db < 4; ++db) vf[db] = vread(vp + 32 * db);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int bt = 0; bt < 4; ++bt) {
+      bf16x8 vn[4];
+      if (bt < 3) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * b + 16 * t);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[b][t], o[db], 0, 0, 0);
-        }
+        for (int db = 0; db < 4; ++db) vn[db] = vread(vp + (16 * (bt + 1)) * kVStride + 32 * db);
+      }
+      const uint4 w = make_uint4(pw[4 * bt], pw[4 * bt + 1], pw[4 * bt + 2], pw[4 * bt + 3]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], __builtin_bit_cast(bf16x8, w), o[db], 0, 0, 0);
+      if (bt < 3) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vf[db] = vn[db];
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next k-step's V reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);     // 4 MFMAs
     }
-
-    if (kt + 1 < n_kt) lstore(buf ^ 1);
+    store_rows(k_lds[kt & 1], kKStride, *reinterpret_cast<uint4(*)[2]>(&st_store[0]));
+    store_rows(v_lds[(kt + 1) & 1], kVStride, *reinterpret_cast<uint4(*)[2]>(&st_store[2]));
     __syncthreads();
+  };
+
+  int kt = 0;
+  for (; kt + 1 < n_kt; kt += 2) {
+    step(kt, s_a, s_b, stage0, stage1);
+    step(kt + 1, s_b, s_a, stage1, stage0);
   }
+  if (kt < n_kt) step(kt, s_a, s_b, stage0, stage1);
+  const float l_run = l_run0 + l_run1;
 
   // Epilogue: full row sum, normalise, round once to bf16.
-  l_run += __shfl_xor(l_run, 32);
-  const float inv_l = 1.0f / l_run;
-  if (qvalid) {
+  const float inv_l = 1.0f / lane_half_sum(l_run);
+  if (qrow < L) {
     uint16_t *orow = O + head_off + static_cast<size_t>(qrow) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)

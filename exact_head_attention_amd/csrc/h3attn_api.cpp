@@ -81,7 +81,7 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
   const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
     return H3_ERR_ALIAS;
-  if (h3::attention_grid(H, L) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
+  if (L > H3ATTN_MAX_ATTENTION_L || h3::attention_grid(H, L) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
   hipError_t e = h3::launch_attention(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                       static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out),
                                       H, L, scale, static_cast<hipStream_t>(stream));

@@ -40,6 +40,8 @@ extern "C" {
 
 #define H3ATTN_ABI_VERSION 1
 #define H3ATTN_HEAD_DIM 128
+/* Longest sequence h3_attention takes: one head's K or V must stay below 2 GiB. */
+#define H3ATTN_MAX_ATTENTION_L (1 << 23)
 
 typedef enum {
   H3_OK = 0,
@@ -83,7 +85,8 @@ int h3_qknorm_rope(void *q, void *k, const float *gamma_q, const float *gamma_k,
  *   out[h][i][:] = sum_j softmax_j(scale * <q[h][i], k[h][j]>) * v[h][j][:]
  * over all L keys of head h.  bf16 inputs, bf16 MFMA products with fp32
  * accumulation, online softmax in fp32, output rounded once to bf16.  Any
- * L >= 1 is accepted; a partial last tile is predicated, never padded.
+ * 1 <= L <= H3ATTN_MAX_ATTENTION_L is accepted; a partial last tile is
+ * predicated, never padded.
  *
  *   q, k, v       bf16 [H][L][D], read only.
  *   out           bf16 [H][L][D], written; must not overlap q, k or v.

@@ -64,6 +64,7 @@ def test_attention_argument_errors(B):
     assert _attn(B, q=None) == -1 and _attn(B, o=None) == -1
     assert _attn(B, H=0) == -2 and _attn(B, L=0) == -2 and _attn(B, L=-5) == -2
     assert _attn(B, H=1 << 16, L=1 << 16) == -2
+    assert _attn(B, H=1, L=(1 << 23) + 1) == -2
     assert _attn(B, D=64) == -3 and _attn(B, D=129) == -3
     assert _attn(B, q=A + 8) == -4 and _attn(B, o=A + 192 * MB + 2) == -4
     assert _attn(B, o=A + 64 * MB + 16) == -5              # out overlaps k
