@@ -20,6 +20,13 @@ LIB = os.path.join(PKG, "libh3attn.so")
 
 SOURCES = ["h3attn_api.cpp", "qknorm_rope.hip", "attn_fwd.hip"]
 
+# Per-source device flags.  The attention kernel assumes finite inputs (the
+# ABI documents it), so the NaN-quieting that max() otherwise needs is
+# dropped; infinities are still honoured (masked keys are -inf).
+SOURCE_FLAGS = {
+    "attn_fwd.hip": ["-fno-honor-nans"],
+}
+
 # Packed-fp32 VALU forms are switched off for all device code.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -35,10 +42,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libh3attn.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,6 +52,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        _run([hipcc(), *compile_flags, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE,
+              "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

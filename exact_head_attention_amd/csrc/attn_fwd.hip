@@ -98,6 +98,19 @@ __device__ __forceinline__ float lane_half_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// Max of 32 scores (two 16-value accumulators), as a tree of independent maxes.
+__device__ __forceinline__ float max32(const f32x16 &a, const f32x16 &b) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    t[i] = __builtin_fmaxf(__builtin_fmaxf(a[2 * i], a[2 * i + 1]), __builtin_fmaxf(b[2 * i], b[2 * i + 1]));
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = __builtin_fmaxf(t[i], t[i + w]);
+  return t[0];
+}
+
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, int L, int n_qtiles, float scale_log2e) {
@@ -224,12 +237,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i)
           if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= L) s_cur[b][i] = -__builtin_inff();
     }
-    float mx = s_cur[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = __builtin_fmaxf(mx, s_cur[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s_cur[1][i]);
-    const float mxs = lane_half_max(mx) * scale_log2e;
+    const float mxs = lane_half_max(max32(s_cur[0], s_cur[1])) * scale_log2e;
     if (__builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mxs);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);

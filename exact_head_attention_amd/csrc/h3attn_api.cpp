@@ -74,14 +74,14 @@ int h3_qknorm_rope(void *q, void *k, const float *gamma_q, const float *gamma_k,
 int h3_attention(const void *q, const void *k, const void *v, void *out,
                  int H, int L, int D, float scale, void *stream) {
   if (!q || !k || !v || !out) return H3_ERR_NULL;
-  if (!shape_ok(H, L)) return H3_ERR_SHAPE;
+  if (!shape_ok(H, L) || L > H3ATTN_MAX_ATTENTION_L || h3::attention_grid(H, L) >= (int64_t{1} << 31))
+    return H3_ERR_SHAPE;
   if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return H3_ERR_ALIGN;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
   const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
     return H3_ERR_ALIAS;
-  if (L > H3ATTN_MAX_ATTENTION_L || h3::attention_grid(H, L) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
   hipError_t e = h3::launch_attention(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                       static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out),
                                       H, L, scale, static_cast<hipStream_t>(stream));
