@@ -50,11 +50,11 @@ constexpr int kBc = 64;              // keys per tile
 constexpr int kKStride = D + 8;      // bf16 per K row in LDS (272 B: rows shift 4 banks)
 constexpr int kVStride = D + 32;     // bf16 per V row in LDS (320 B: transpose reads hit 4 disjoint bank windows)
 constexpr float kLog2e = 1.4426950408889634f;
-// The running max is raised only when a tile's max exceeds it by more than
-// kTau (base-2 units), so unnormalised weights stay <= 2^kTau = 256 (exact in
-// bf16's range; fp32 sums).  Any offset cancels between numerator and
-// denominator, so this changes rounding only, never the result's definition.
-constexpr float kTau = 8.0f;
+// The running max is raised only when some row of the wave sees a larger
+// score (a wave-uniform branch, taken a few dozen times per 32-row block over
+// a 32k sequence), so the O rescale is skipped on almost every tile.  The max
+// is always exact: a row's largest weight is then exactly 1, which keeps the
+// bf16 rounding of P off the dominant term of peaky rows.
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data, gfx9 encoding
 
 __device__ __forceinline__ int swap_bits23(int m) {
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
           if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= L) s_cur[b][i] = -__builtin_inff();
     }
     const float mxs = lane_half_max(max32(s_cur[0], s_cur[1])) * scale_log2e;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mxs);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
