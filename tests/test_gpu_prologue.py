@@ -36,6 +36,15 @@ def test_rope_tables_match_oracle(gpu_lib, name):
 
 
 def _prologue_check(gpu_lib, x, label):
+    """Every element against the exact fp64 value y of the oracle.
+
+    The GPU computes in fp32 and rounds once to bf16 (the ABI's definition), so
+    an element may differ from y by one bf16 spacing (rounding of a slightly
+    different fp32 value) plus the fp32 arithmetic error.  That error scales
+    with the terms being combined, not with the result: where the rotation
+    cancels (y2j*c - y2j+1*s << its terms) it can exceed one spacing of the
+    small result.  A few fp32 roundings of terms bounded by the row's largest
+    |y| give the 2^-18 * max_row|y| slack."""
     import torch
     d = device_inputs(x)
     cos, sin = gpu_lib.rope_tables(d["positions"], 128, x["theta"])
@@ -45,11 +54,17 @@ def _prologue_check(gpu_lib, x, label):
     for nm, gname in (("q", "gamma_q"), ("k", "gamma_k")):
         got = bits(d[nm])
         y, yb = oracle.qknorm_rope(x[nm], x[gname], c_ref, s_ref, x["eps"])
+        g64 = oracle.bf16_to_f64(got)
+        mag = np.abs(y)
+        spacing = np.exp2(np.maximum(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7, -133))
+        slack = spacing + 2.0 ** -18 * mag.max(axis=-1, keepdims=True)
+        err = np.abs(g64 - y)
         ulps = bf16_ulp_distance(got, yb)
         frac = float(np.mean(got != yb))
         rel = row_rel_err(got.reshape(-1, 128), y.reshape(-1, 128))
-        print(f"{label} {nm}: max ulp {ulps.max():.0f}, mismatching {frac:.2e}, max row rel {rel.max():.2e}")
-        assert ulps.max() <= 1.0
+        print(f"{label} {nm}: max ulp vs RNE(ref) {ulps.max():.0f} (elements > 1 ulp: {int((ulps > 1).sum())}), "
+              f"mismatching {frac:.2e}, max err/slack {float((err / slack).max()):.3f}, max row rel {rel.max():.2e}")
+        assert np.all(err <= slack)
         assert frac < 2e-3
         assert rel.max() <= 4e-3
 
