@@ -12,4 +12,6 @@ from .h3_oracle import (  # noqa: F401
     qknorm_rope,
     attention_head,
     attention,
+    attention_lse_head,
+    merge_partials,
 )

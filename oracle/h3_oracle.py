@@ -25,6 +25,14 @@ What it computes (sources are the three pages the build follows):
   plain definition; the GPU's tiled online softmax reaches the same value up to
   rounding.
 
+* Partial attention over a key range with its log-sum-exp, and the merge of
+  such partials.  The pages' next scaling axis past the 56-head Ulysses cap is
+  context/ring parallelism over K/V blocks ("Tensor parallelism for
+  MiniMax-H3", whn09's comments on the ceiling and on TP x CP meshes); its
+  building block is exact: lse = log sum_j exp(scale * q.k_j) over the range,
+  and parts combine as out = sum_p exp(lse_p - lse) out_p with
+  lse = log sum_p exp(lse_p).
+
 Every pin of these functions lives in tests/test_oracle.py.  One part is
 parity unpinned: whether the adjacent-pair RoPE convention and the fp64 tables
 match the real MiniMax-H3 checkpoint (no page states it; the GPU kernel takes
@@ -167,3 +175,46 @@ def attention(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         v = bf16_to_f64(v_bits[h])
         outs.append(attention_head(q, k, v, scale))
     return np.stack(outs)
+
+
+# --------------------------------------------------------------------------
+# Partial attention with log-sum-exp, and the merge of partials
+# --------------------------------------------------------------------------
+
+
+def attention_lse_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, block: int = 256):
+    """(out, lse) for one head over the given keys, in fp64.
+
+    out = softmax(scale * q k^T) v as in attention_head; lse[r] is the natural
+    log of sum_j exp(scale * <q_r, k_j>), computed as m + log(sum exp(s - m)).
+    """
+    import torch
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64))
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64))
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))
+    out = torch.empty((qt.shape[0], vt.shape[1]), dtype=torch.float64)
+    lse = torch.empty(qt.shape[0], dtype=torch.float64)
+    for r0 in range(0, qt.shape[0], block):
+        s = float(scale) * (qt[r0:r0 + block] @ kt.T)
+        m = s.max(dim=1, keepdim=True).values
+        e = torch.exp(s - m)
+        z = e.sum(dim=1, keepdim=True)
+        out[r0:r0 + block] = (e / z) @ vt
+        lse[r0:r0 + block] = (m + torch.log(z))[:, 0]
+    return out.numpy(), lse.numpy()
+
+
+def merge_partials(outs: np.ndarray, lses: np.ndarray):
+    """Combine P partial results over disjoint key ranges.
+
+    outs [P, ..., D], lses [P, ...]: lse = log sum_p exp(lse_p) (max-shifted),
+    out = sum_p exp(lse_p - lse) * out_p.  Returns (out, lse) in fp64.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    m = lses.max(axis=0)
+    w = np.exp(lses - m[None])
+    z = w.sum(axis=0)
+    lse = m + np.log(z)
+    out = (w[..., None] * outs).sum(axis=0) / z[..., None]
+    return out, lse

@@ -377,3 +377,61 @@ def test_attention_block_size_does_not_change_rows():
     a = O.attention_head(q, k, v, 0.1, block=256)
     b = O.attention_head(q, k, v, 0.1, block=7)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------ log-sum-exp and merging
+
+
+def test_lse_closed_forms():
+    """Closed forms: one key gives lse = scale*<q,k>; L identical keys give
+    scale*<q,k> + ln L; the output part equals attention_head's."""
+    rng = np.random.default_rng(20)
+    q, k1 = rng.standard_normal((3, 128)), rng.standard_normal((1, 128))
+    v1 = rng.standard_normal((1, 128))
+    out, lse = O.attention_lse_head(q, k1, v1, 0.3)
+    np.testing.assert_allclose(lse, 0.3 * (q @ k1[0]), rtol=1e-13)
+    assert np.array_equal(out, np.tile(v1, (3, 1)))
+    kk = np.tile(k1, (50, 1))
+    _, lse50 = O.attention_lse_head(q, kk, rng.standard_normal((50, 128)), 0.3)
+    np.testing.assert_allclose(lse50, 0.3 * (q @ k1[0]) + math.log(50), rtol=1e-13)
+    k, v = rng.standard_normal((77, 128)), rng.standard_normal((77, 128))
+    out, _ = O.attention_lse_head(q, k, v, 0.1)
+    np.testing.assert_allclose(out, O.attention_head(q, k, v, 0.1), rtol=1e-13, atol=1e-15)
+
+
+def test_lse_vs_scipy_logsumexp():
+    """Library: scipy.special.logsumexp of the scaled scores, including logits
+    large enough that an unshifted exp would overflow."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    q, k = rng.standard_normal((9, 128)) * 40, rng.standard_normal((300, 128)) * 40
+    _, lse = O.attention_lse_head(q, k, rng.standard_normal((300, 128)), 1 / math.sqrt(128))
+    np.testing.assert_allclose(lse, logsumexp(q @ k.T / math.sqrt(128), axis=1), rtol=1e-12)
+
+
+def test_merge_of_split_equals_unsplit():
+    """Invariant: attention over keys split into ranges, merged, equals the
+    attention over all keys (outputs and lse), for uneven splits."""
+    rng = np.random.default_rng(22)
+    q, k, v = rng.standard_normal((40, 128)), rng.standard_normal((500, 128)), rng.standard_normal((500, 128))
+    s = 1 / math.sqrt(128)
+    full, lse_full = O.attention_lse_head(q, k, v, s)
+    cuts = [0, 7, 200, 201, 500]
+    parts = [O.attention_lse_head(q, k[a:b], v[a:b], s) for a, b in zip(cuts, cuts[1:])]
+    out, lse = O.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    np.testing.assert_allclose(out, full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full, rtol=1e-13)
+
+
+def test_merge_single_part_and_empty_part():
+    """Special cases: one part is returned unchanged; a part with lse = -inf
+    (no keys) contributes nothing."""
+    rng = np.random.default_rng(23)
+    o1, l1 = rng.standard_normal((2, 5, 128)), rng.standard_normal((2, 5))
+    out, lse = O.merge_partials(o1[None], l1[None])
+    np.testing.assert_allclose(out, o1, rtol=1e-15)
+    np.testing.assert_allclose(lse, l1, rtol=1e-15)
+    out2, lse2 = O.merge_partials(np.stack([o1, rng.standard_normal((2, 5, 128))]),
+                                  np.stack([l1, np.full((2, 5), -np.inf)]))
+    np.testing.assert_allclose(out2, o1, rtol=1e-15)
+    np.testing.assert_allclose(lse2, l1, rtol=1e-15)

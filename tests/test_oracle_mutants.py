@@ -90,6 +90,18 @@ def _attn_softmax_over_queries(q, k, v, scale, block=256):
     return (e / e.sum(axis=0, keepdims=True)) @ v
 
 
+def _merge_linear_weights(outs, lses):
+    outs, lses = np.asarray(outs, np.float64), np.asarray(lses, np.float64)
+    w = lses - lses.min(axis=0)[None] + 1.0
+    return (w[..., None] * outs).sum(axis=0) / w.sum(axis=0)[..., None], np.log(np.exp(lses).sum(axis=0))
+
+
+def _lse_missing_log(q, k, v, scale, block=256):
+    out, lse = H.__dict__["_orig_attention_lse_head"](q, k, v, scale, block)
+    s = scale * (np.asarray(q) @ np.asarray(k).T)
+    return out, s.max(axis=1) + np.exp(lse - s.max(axis=1))
+
+
 PIN_TESTS = [getattr(T, n) for n in dir(T) if n.startswith("test_")]
 
 MUTANTS = {
@@ -106,6 +118,8 @@ MUTANTS = {
     "attn_unnormalised": ("attention_head", _attn_unnormalised),
     "attn_no_max_shift": ("attention_head", _attn_no_max),
     "attn_softmax_wrong_axis": ("attention_head", _attn_softmax_over_queries),
+    "merge_linear_weights": ("merge_partials", _merge_linear_weights),
+    "lse_missing_log": ("attention_lse_head", _lse_missing_log),
 }
 
 
@@ -113,6 +127,7 @@ MUTANTS = {
 def test_pins_catch_mutant(name, monkeypatch):
     fn_name, mutant = MUTANTS[name]
     monkeypatch.setitem(H.__dict__, "_orig_attention_head", H.attention_head)
+    monkeypatch.setitem(H.__dict__, "_orig_attention_lse_head", H.attention_lse_head)
     monkeypatch.setattr(H, fn_name, mutant)
     monkeypatch.setattr(oracle, fn_name, mutant)
     failed = []
