@@ -27,13 +27,19 @@ lib.h3_attention.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _f, _vp]
 lib.h3_attention.restype = _i
 lib.h3_rope_tables.argtypes = [_vp, _i, _i, _d, _vp, _vp, _vp]
 lib.h3_rope_tables.restype = _i
+_ll = ctypes.c_longlong
+lib.h3_attention_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _ll, _i, _f, _vp]
+lib.h3_attention_lse.restype = _i
+lib.h3_attention_merge.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp]
+lib.h3_attention_merge.restype = _i
 lib.h3_status_string.argtypes = [_i]
 lib.h3_status_string.restype = ctypes.c_char_p
 lib.h3_abi_version.argtypes = []
 lib.h3_abi_version.restype = _i
 
 HEAD_DIM = 128
-EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_status_string", "h3_abi_version")
+EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
+            "h3_status_string", "h3_abi_version")
 
 
 class H3Error(RuntimeError):
@@ -114,3 +120,52 @@ def attention(q, k, v, out=None, scale: float | None = None):
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         _dev(out, torch.bfloat16, "out"), H, L, D, float(scale), _stream()))
     return out
+
+
+def _kv_view(t, name):
+    """Pointer and head stride of a key/value tensor [H, Lk, D] whose rows are
+    contiguous (e.g. a key-range slice t_full[:, j0:j1] of a [H, L, D] tensor)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bf16 GPU tensor")
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+        raise ValueError(f"{name} must be [H, Lk, {HEAD_DIM}] with contiguous rows")
+    return ctypes.c_void_p(t.data_ptr()), int(t.stride(0)) if t.shape[0] > 1 else t.shape[1] * HEAD_DIM
+
+
+def attention_lse(q, k, v, scale: float | None = None, out=None, lse=None):
+    """Partial attention of q over the keys in k, v (which may be a key-range
+    slice of a larger tensor).  Returns (out fp32 [H, Lq, 128], lse fp32 [H, Lq])."""
+    import torch
+    H, Lq, D = _hld(q, "q")
+    pk, sk = _kv_view(k, "k")
+    pv, sv = _kv_view(v, "v")
+    if k.shape != v.shape or k.shape[0] != H or sk != sv:
+        raise ValueError("k and v must have the same shape and head stride, with q's head count")
+    Lk = k.shape[1]
+    if out is None:
+        out = torch.empty((H, Lq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((H, Lq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("h3_attention_lse", lib.h3_attention_lse(
+        _dev(q, torch.bfloat16, "q"), pk, pv, _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse"),
+        H, Lq, Lk, sk, D, float(scale), _stream()))
+    return out, lse
+
+
+def attention_merge(outs, lses, out=None, want_lse: bool = False):
+    """Merge stacked partials outs fp32 [P, H, L, 128], lses fp32 [P, H, L]
+    into bf16 [H, L, 128] (and the merged lse when want_lse)."""
+    import torch
+    if outs.dim() != 4 or outs.shape[3] != HEAD_DIM or tuple(lses.shape) != tuple(outs.shape[:3]):
+        raise ValueError("outs must be [P, H, L, 128] and lses [P, H, L]")
+    P, H, L, D = outs.shape
+    if out is None:
+        out = torch.empty((H, L, D), dtype=torch.bfloat16, device=outs.device)
+    lse_out = torch.empty((H, L), dtype=torch.float32, device=outs.device) if want_lse else None
+    _check("h3_attention_merge", lib.h3_attention_merge(
+        _dev(outs, torch.float32, "outs"), _dev(lses, torch.float32, "lses"), P, _dev(out, torch.bfloat16, "out"),
+        _dev(lse_out, torch.float32, "lse_out") if want_lse else None, H, L, D, _stream()))
+    return (out, lse_out) if want_lse else out

@@ -111,9 +111,16 @@ __device__ __forceinline__ float max32(const f32x16 &a, const f32x16 &b) {
   return t[0];
 }
 
+// kLse = false: out = softmax(scale q k^T) v rounded to bf16 (h3_attention).
+// kLse = true:  out_f32 = the same normalised result in fp32 and lse = the
+// natural log of sum_j exp(scale q.k_j) over the Lk keys given (the partial
+// form h3_attention_merge combines).  Queries: [H][Lq][D]; keys and values:
+// element (h, j, d) at h*kv_stride + j*D + d, j < Lk.
+template <bool kLse>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    uint16_t *__restrict__ O, int L, int n_qtiles, float scale_log2e) {
+    uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
+    long long kv_stride, int n_qtiles, float scale_log2e) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBc * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBc * kVStride];
 
@@ -124,17 +131,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int head = logical / n_qtiles;
   const int qt = logical - head * n_qtiles;
-  const size_t head_off = static_cast<size_t>(head) * L * D;
+  const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Qh = Q + head_off;
-  const uint16_t *Kh = K + head_off;
-  const uint16_t *Vh = V + head_off;
+  const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
+  const uint16_t *Vh = V + static_cast<size_t>(head) * kv_stride;
   const int row_bytes = D * 2;
 
   // Q^T fragments (B operand): lane holds query row qrow, d = 16c + 8g .. +7.
   const int qrow = qt * kBr + wave * 32 + l32;
   bf16x8 qf[8];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, L * row_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, Lq * row_bytes);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, qrow * row_bytes + 32 * c + 16 * g));
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   // V; thread takes chunks tid and tid + 512 (tile-relative byte offset
   // chunk * 16).  Both land row-major in LDS.
   auto load_kv = [&](const uint16_t *base, int kt, uint4 (&r)[2]) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (L - kt * kBc) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (Lk - kt * kBc) * row_bytes);
     r[0] = bload128(rs, tid * 16);
     r[1] = bload128(rs, (tid + kThreads) * 16);
   };
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   float m_run = -__builtin_inff();  // running max, base-2 scaled units
   float l_run0 = 0.f, l_run1 = 0.f; // this lane's partial row sums of the bf16 weights
 
-  const int n_kt = (L + kBc - 1) / kBc;
+  const int n_kt = (Lk + kBc - 1) / kBc;
   // Staging registers, two sets: a step stores the set loaded one step
   // earlier and refills the other, so global-load latency hides behind a
   // whole step.  Set layout: [0..1] K chunks, [2..3] V chunks.
@@ -230,12 +237,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     // (1) Mask the ragged tail, row max, and (rarely) raise the running max.
     // s_cur[b][i] holds key kt*64 + 32b + 16(i/8) + 8g + i%8.
     const int key_base = kt * kBc;
-    if (key_base + kBc > L) {
+    if (key_base + kBc > Lk) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= L) s_cur[b][i] = -__builtin_inff();
+          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= Lk) s_cur[b][i] = -__builtin_inff();
     }
     const float mxs = lane_half_max(max32(s_cur[0], s_cur[1])) * scale_log2e;
     if (__builtin_amdgcn_ballot_w64(mxs > m_run) != 0) {
@@ -327,9 +334,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   if (kt < n_kt) step(kt, s_a, s_b, stage0, stage1);
   const float l_run = l_run0 + l_run1;
 
-  // Epilogue: full row sum, normalise, round once to bf16.
-  const float inv_l = 1.0f / lane_half_sum(l_run);
-  if (qrow < L) {
+  // Epilogue: full row sum, normalise, round once to bf16 (or keep fp32 and
+  // write the log-sum-exp: ln(l * 2^m) = (log2(l) + m) * ln 2).
+  const float l_tot = lane_half_sum(l_run);
+  const float inv_l = 1.0f / l_tot;
+  if (kLse && qrow < Lq) {
+    float *orow = O32 + head_off + static_cast<size_t>(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        *reinterpret_cast<float4 *>(orow + 32 * db + 8 * grp + 4 * g) =
+            make_float4(o[db][4 * grp + 0] * inv_l, o[db][4 * grp + 1] * inv_l, o[db][4 * grp + 2] * inv_l,
+                        o[db][4 * grp + 3] * inv_l);
+    if (g == 0)
+      lse_out[static_cast<size_t>(head) * Lq + qrow] = (__builtin_amdgcn_logf(l_tot) + m_run) * 0.69314718055994531f;
+  }
+  if (!kLse && qrow < Lq) {
     uint16_t *orow = O + head_off + static_cast<size_t>(qrow) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -354,8 +375,56 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int L, float scale, hipStream_t stream) {
   const int n_qtiles = (L + kBr - 1) / kBr;
   const int blocks = static_cast<int>(attention_grid(H, L));
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(blocks), dim3(kThreads), 0, stream, q, k, v, out, L, n_qtiles,
-                     scale * kLog2e);
+  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v, out, nullptr,
+                     nullptr, L, L, static_cast<long long>(L) * D, n_qtiles, scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
+                                int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
+  const int n_qtiles = (Lq + kBr - 1) / kBr;
+  const int blocks = static_cast<int>(attention_grid(H, Lq));
+  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v, nullptr, out, lse,
+                     Lq, Lk, kv_stride, n_qtiles, scale * kLog2e);
+  return hipGetLastError();
+}
+
+// Merge of P partial results: one 32-lane half-wave per (head, row); lane
+// holds 4 of the 128 columns.  lse = m + log(sum_p exp(lse_p - m)), out =
+// sum_p exp(lse_p - lse) * out_p, rounded once to bf16.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ outs,
+                                                         const float *__restrict__ lses, int P, long long rows,
+                                                         uint16_t *__restrict__ out, float *__restrict__ lse_out) {
+  const long long row = static_cast<long long>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 4;
+  if (row >= rows) return;
+  float m = -__builtin_inff();
+  for (int p = 0; p < P; ++p) m = __builtin_fmaxf(m, lses[p * rows + row]);
+  float z = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < P; ++p) {
+    const float w = (m == -__builtin_inff()) ? 0.f : __expf(lses[p * rows + row] - m);
+    const float4 x = *reinterpret_cast<const float4 *>(outs + (p * rows + row) * D + c);
+    z += w;
+    acc.x = __builtin_fmaf(w, x.x, acc.x);
+    acc.y = __builtin_fmaf(w, x.y, acc.y);
+    acc.z = __builtin_fmaf(w, x.z, acc.z);
+    acc.w = __builtin_fmaf(w, x.w, acc.w);
+  }
+  const float inv = 1.0f / z;
+  uint2 wv;
+  wv.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  wv.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2 *>(out + row * D + c) = wv;
+  if (lse_out != nullptr && c == 0) lse_out[row] = m + __logf(z);
+}
+
+hipError_t launch_attention_merge(const float *outs, const float *lses, int P, uint16_t *out, float *lse_out,
+                                  int H, int L, hipStream_t stream) {
+  const long long rows = static_cast<long long>(H) * L;
+  const long long blocks = (rows + 7) / 8;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, outs, lses, P,
+                     rows, out, lse_out);
   return hipGetLastError();
 }
 

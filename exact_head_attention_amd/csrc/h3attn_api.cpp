@@ -11,6 +11,7 @@
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Byte ranges [a, a+na) and [b, b+nb) overlap.
 bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
@@ -85,6 +86,53 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
   hipError_t e = h3::launch_attention(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                       static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out),
                                       H, L, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_attention_lse(const void *q, const void *k, const void *v, float *out, float *lse, int H, int Lq,
+                     int Lk, long long kv_head_stride, int D, float scale, void *stream) {
+  if (!q || !k || !v || !out || !lse) return H3_ERR_NULL;
+  if (!shape_ok(H, Lq) || Lk < 1 || Lq > H3ATTN_MAX_ATTENTION_L || Lk > H3ATTN_MAX_ATTENTION_L ||
+      h3::attention_grid(H, Lq) >= (int64_t{1} << 31) || kv_head_stride < static_cast<long long>(Lk) * D ||
+      kv_head_stride > (int64_t{1} << 40))
+    return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(lse) ||
+      (kv_head_stride % 8) != 0)
+    return H3_ERR_ALIGN;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  const uint64_t q_bytes = static_cast<uint64_t>(H) * Lq * D * 2;
+  const uint64_t kv_bytes = (static_cast<uint64_t>(H - 1) * kv_head_stride + static_cast<uint64_t>(Lk) * D) * 2;
+  const uint64_t out_bytes = static_cast<uint64_t>(H) * Lq * D * 4;
+  const uint64_t lse_bytes = static_cast<uint64_t>(H) * Lq * 4;
+  if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k, kv_bytes) ||
+      overlaps(out, out_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
+      overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
+      overlaps(lse, lse_bytes, out, out_bytes))
+    return H3_ERR_ALIAS;
+  hipError_t e = h3::launch_attention_lse(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                          static_cast<const uint16_t *>(v), out, lse, H, Lq, Lk, kv_head_stride,
+                                          scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_attention_merge(const float *outs, const float *lses, int P, void *out, float *lse_out, int H, int L,
+                       int D, void *stream) {
+  if (!outs || !lses || !out) return H3_ERR_NULL;
+  if (P < 1 || !shape_ok(H, L) || static_cast<int64_t>(P) * H * L >= (int64_t{1} << 40)) return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if (!aligned16(outs) || !aligned4(lses) || !aligned16(out) || (lse_out && !aligned4(lse_out)))
+    return H3_ERR_ALIGN;
+  const uint64_t rows = static_cast<uint64_t>(H) * L;
+  const uint64_t outs_bytes = static_cast<uint64_t>(P) * rows * D * 4;
+  const uint64_t lses_bytes = static_cast<uint64_t>(P) * rows * 4;
+  const uint64_t out_bytes = rows * D * 2;
+  if (overlaps(out, out_bytes, outs, outs_bytes) || overlaps(out, out_bytes, lses, lses_bytes)) return H3_ERR_ALIAS;
+  if (lse_out && (overlaps(lse_out, rows * 4, outs, outs_bytes) || overlaps(lse_out, rows * 4, lses, lses_bytes) ||
+                  overlaps(lse_out, rows * 4, out, out_bytes)))
+    return H3_ERR_ALIAS;
+  hipError_t e = h3::launch_attention_merge(outs, lses, P, static_cast<uint16_t *>(out), lse_out, H, L,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 

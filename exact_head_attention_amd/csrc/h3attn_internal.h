@@ -24,4 +24,10 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, uint16_t *out, int H, int L,
                             float scale, hipStream_t stream);
 
+hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
+                                int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream);
+
+hipError_t launch_attention_merge(const float *outs, const float *lses, int P, uint16_t *out, float *lse_out,
+                                  int H, int L, hipStream_t stream);
+
 }  // namespace h3

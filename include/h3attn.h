@@ -97,6 +97,47 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
                  int H, int L, int D, float scale, void *stream);
 
 /*
+ * Partial attention over a range of keys, with its log-sum-exp: the building
+ * block for splitting the keys of one head across launches or devices
+ * (context/ring parallelism, which "Tensor parallelism for MiniMax-H3" names,
+ * in whn09's comments, as the next axis past the head-count cap on Ulysses).
+ * For every head h and query row i:
+ *   out[h][i][:] = sum_j softmax_j(scale * <q[h][i], k_h[j]>) * v_h[j][:]
+ *   lse[h][i]    = ln sum_j exp(scale * <q[h][i], k_h[j]>)
+ * over the Lk keys j of this range only, with out kept in fp32 (normalised
+ * within the range) so that h3_attention_merge can combine ranges exactly.
+ *
+ *   q             bf16 [H][Lq][D].
+ *   k, v          bf16; element (h, j, d) at h*kv_head_stride + j*D + d,
+ *                 j < Lk.  A key range [j0, j0+Lk) of a [H][L][D] tensor is
+ *                 k + j0*D with kv_head_stride = L*D.
+ *   out           fp32 [H][Lq][D], written.      lse  fp32 [H][Lq], written.
+ *   Lq, Lk        1 .. H3ATTN_MAX_ATTENTION_L;  kv_head_stride >= Lk*D and a
+ *                 multiple of 8 elements.
+ *   scale         > 0 and finite.
+ * q, k, v, out must be 16-byte aligned; out and lse must not overlap the
+ * inputs or each other.  Bit-identical per head for any head split.
+ */
+int h3_attention_lse(const void *q, const void *k, const void *v, float *out, float *lse,
+                     int H, int Lq, int Lk, long long kv_head_stride, int D, float scale,
+                     void *stream);
+
+/*
+ * Combines P partial results over disjoint key ranges of the same queries:
+ *   lse = ln sum_p exp(lse_p),   out = sum_p exp(lse_p - lse) * out_p,
+ * with out rounded once to bf16 (a part with lse_p = -inf contributes 0).
+ *
+ *   outs          fp32 [P][H][L][D] (h3_attention_lse outputs, stacked).
+ *   lses          fp32 [P][H][L].
+ *   out           bf16 [H][L][D], written.
+ *   lse_out       fp32 [H][L], written; may be NULL.
+ * outs and out must be 16-byte aligned, lses and lse_out 4-byte aligned;
+ * outputs must not overlap inputs.
+ */
+int h3_attention_merge(const float *outs, const float *lses, int P, void *out, float *lse_out,
+                       int H, int L, int D, void *stream);
+
+/*
  * Rotary tables for h3_qknorm_rope:
  *   inv_freq_j = theta^(-2j/D),  angle = positions[i] * inv_freq_j,
  *   cos[i][j] = cos(angle), sin[i][j] = sin(angle),   j = 0 .. D/2-1,

@@ -24,7 +24,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_status_string", "h3_abi_version"):
+    for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
+              "h3_status_string", "h3_abi_version"):
         assert n in names
 
 
@@ -99,3 +100,34 @@ def test_binding_rejects_cpu_tensors(B):
         B.attention(q, q, q)
     with pytest.raises(ValueError):
         B.attention(torch.zeros(1, 4, 64, dtype=torch.bfloat16), q, q)
+
+
+def _lse(B, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 320 * MB, H=2, Lq=512, Lk=256,
+         stride=512 * 128, D=128, scale=0.088):
+    return B.lib.h3_attention_lse(q, k, v, o, lse, H, Lq, Lk, stride, D, scale, None)
+
+
+def _merge(B, outs=A, lses=A + 64 * MB, P=3, out=A + 128 * MB, lse_out=A + 192 * MB, H=2, L=512, D=128):
+    return B.lib.h3_attention_merge(outs, lses, P, out, lse_out, H, L, D, None)
+
+
+def test_attention_lse_argument_errors(B):
+    assert _lse(B, q=None) == -1 and _lse(B, lse=None) == -1 and _lse(B, o=None) == -1
+    assert _lse(B, H=0) == -2 and _lse(B, Lq=0) == -2 and _lse(B, Lk=0) == -2
+    assert _lse(B, Lk=(1 << 23) + 1, stride=((1 << 23) + 1) * 128) == -2
+    assert _lse(B, stride=255 * 128) == -2                 # head stride shorter than Lk rows
+    assert _lse(B, D=64) == -3
+    assert _lse(B, k=A + 64 * MB + 8) == -4 and _lse(B, lse=A + 320 * MB + 2) == -4
+    assert _lse(B, stride=512 * 128 + 4) == -4             # head bases lose 16-byte alignment
+    assert _lse(B, scale=0.0) == -6 and _lse(B, scale=float("nan")) == -6
+    assert _lse(B, o=A + 64 * MB) == -5                    # out over k
+    assert _lse(B, lse=A + 192 * MB + 16) == -5            # lse inside out
+
+
+def test_attention_merge_argument_errors(B):
+    assert _merge(B, outs=None) == -1 and _merge(B, out=None) == -1
+    assert _merge(B, P=0) == -2 and _merge(B, H=0) == -2 and _merge(B, L=0) == -2
+    assert _merge(B, D=256) == -3
+    assert _merge(B, outs=A + 4) == -4 and _merge(B, lse_out=A + 192 * MB + 1) == -4
+    assert _merge(B, out=A + 16) == -5                     # out inside outs
+    assert _merge(B, lse_out=A + 128 * MB) == -5           # lse_out over out

@@ -1,0 +1,115 @@
+"""GPU parity of h3_attention_lse and h3_attention_merge against the oracle.
+
+Partial outputs are fp32 (the only rounding is the bf16 of the attention
+weights, as in h3_attention), so they share the 4e-3 per-row bar.  The
+log-sum-exp is compared absolutely: it is ln(l) + m with l a sum of bf16
+weights, so its error is about the relative error of that sum (<< 1e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_head_attention_amd import inputs as I
+from tests.gpu_helpers import ATTN_TOL, bits, host_inputs, row_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+LSE_TOL = 2e-3
+
+
+def _raw(H, L, seed, mult=1.0):
+    import torch
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [to_dev(I.f32_to_bf16_bits(mult * rng.standard_normal((H, L, 128), dtype=np.float32)), torch.bfloat16)
+            for _ in range(3)]
+
+
+def _rel_rows(got, ref):
+    return np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+
+
+@pytest.mark.parametrize("Lq,j0,j1", [(300, 0, 300), (257, 100, 1000), (64, 999, 1000), (1000, 0, 1)])
+def test_attention_lse_range_vs_oracle(gpu_lib, Lq, j0, j1):
+    """Queries against a key range given as a pointer offset into a larger
+    tensor; out (fp32) and lse against the oracle on every row."""
+    import torch
+    q, _, _ = _raw(2, Lq, seed=31 + Lq)
+    _, kf, vf = _raw(2, 1000, seed=32)
+    s = 1 / math.sqrt(128)
+    out, lse = gpu_lib.attention_lse(q, kf[:, j0:j1], vf[:, j0:j1], scale=s)
+    torch.cuda.synchronize()
+    qb, kb, vb = bits(q), bits(kf), bits(vf)
+    for h in range(2):
+        ref, ref_lse = oracle.attention_lse_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h, j0:j1]),
+                                                 oracle.bf16_to_f64(vb[h, j0:j1]), s)
+        err = _rel_rows(out[h].double().cpu().numpy(), ref)
+        lerr = np.abs(lse[h].double().cpu().numpy() - ref_lse)
+        print(f"Lq={Lq} keys [{j0},{j1}) head {h}: max row rel {err.max():.2e}, max |dlse| {lerr.max():.2e}")
+        assert err.max() <= ATTN_TOL and lerr.max() <= LSE_TOL
+
+
+@pytest.mark.parametrize("cuts", [[0, 500, 1000], [0, 1, 333, 334, 1000], [0, 64, 128, 1000]])
+def test_split_merge_equals_full(gpu_lib, cuts):
+    """Keys split into uneven ranges, partials merged on the GPU: the bf16
+    output and merged lse match the oracle's unsplit attention."""
+    import torch
+    q, k, v = _raw(3, 1000, seed=40, mult=2.0)
+    s = 1 / math.sqrt(128)
+    parts = [gpu_lib.attention_lse(q, k[:, a:b], v[:, a:b], scale=s) for a, b in zip(cuts, cuts[1:])]
+    outs = torch.stack([p[0] for p in parts])
+    lses = torch.stack([p[1] for p in parts])
+    out, lse = gpu_lib.attention_merge(outs, lses, want_lse=True)
+    torch.cuda.synchronize()
+    qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
+    worst = 0.0
+    for h in range(3):
+        ref, ref_lse = oracle.attention_lse_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h]),
+                                                 oracle.bf16_to_f64(vb[h]), s)
+        worst = max(worst, float(row_rel_err(ob[h], ref).max()))
+        assert np.abs(lse[h].double().cpu().numpy() - ref_lse).max() <= LSE_TOL
+    print(f"cuts {cuts}: merged max row rel {worst:.2e}")
+    assert worst <= ATTN_TOL
+
+
+def test_merge_single_part_is_rounding_of_it(gpu_lib):
+    """Special case: merging one part returns its bf16 rounding (RNE) exactly."""
+    import torch
+    q, k, v = _raw(2, 700, seed=41)
+    o32, l32 = gpu_lib.attention_lse(q, k, v)
+    out = gpu_lib.attention_merge(o32[None], l32[None])
+    torch.cuda.synchronize()
+    assert torch.equal(out, o32.to(torch.bfloat16))
+
+
+def test_ws8_two_halves_sampled(gpu_lib):
+    """One rank's workload with its keys split in two halves and merged; 4096
+    sampled rows per head against the oracle."""
+    import torch
+    x = host_inputs("ws8")
+    w = I.WORKLOADS["ws8"]
+    q, k, v = (to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    half = w.L // 2 + 77
+    parts = [gpu_lib.attention_lse(q, k[:, a:b], v[:, a:b], scale=x["scale"]) for a, b in ((0, half), (half, w.L))]
+    out = gpu_lib.attention_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]))
+    torch.cuda.synchronize()
+    qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
+    worst = 0.0
+    for h in range(w.H):
+        rows = I.sample_rows(w, h, 4096)
+        ref = oracle.attention_head(oracle.bf16_to_f64(qb[h, rows]), oracle.bf16_to_f64(kb[h]),
+                                    oracle.bf16_to_f64(vb[h]), x["scale"])
+        worst = max(worst, float(row_rel_err(ob[h, rows], ref).max()))
+    print(f"ws8 split in two and merged: max row rel {worst:.2e}")
+    assert worst <= ATTN_TOL
+
+
+def test_attention_lse_head_splits_bit_identical(gpu_lib):
+    """Per-head determinism of the partial kernel: 4 heads at once vs 2 x 2."""
+    import torch
+    q, k, v = _raw(4, 900, seed=42)
+    o_all, l_all = gpu_lib.attention_lse(q, k[:, 100:800], v[:, 100:800])
+    for h0 in (0, 2):
+        o, l = gpu_lib.attention_lse(q[h0:h0 + 2], k[h0:h0 + 2, 100:800], v[h0:h0 + 2, 100:800])
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_all[h0:h0 + 2]) and torch.equal(l, l_all[h0:h0 + 2])
