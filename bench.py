@@ -226,11 +226,13 @@ def main():
     att_ms_all = [e[1].elapsed_time(e[2]) for e in evs]
     att_ms = float(np.mean(att_ms_all))
 
-    # Prologue alone with the 256 MB last-level cache flushed before each launch.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Prologue alone with the 256 MB last-level cache flushed before each
+    # launch.  The flush only reads (a sum over 512 MiB), so no dirty lines
+    # are still being written back while the timed launch runs.
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
     pro_cold = []
     for _ in range(20):
-        flush.fill_(1)
+        flush.sum(dtype=torch.int32)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         B.qknorm_rope(q, k, gq, gk, cos, sin, x["eps"])

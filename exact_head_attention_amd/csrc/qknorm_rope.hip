@@ -19,6 +19,16 @@
 namespace h3 {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// q and k rows are touched exactly once: stream them past the caches.
+__device__ __forceinline__ uint4 load_stream(const uint16_t *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
+__device__ __forceinline__ void store_stream(uint16_t *p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+
 constexpr int kTokensPerBlock = 16;   // 256 threads = 16 rows of 16 lanes
 constexpr int kHeadUnroll = 4;        // heads whose loads are in flight together
 
@@ -94,15 +104,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
 #pragma unroll
     for (int u = 0; u < kHeadUnroll; ++u) {
       if (h0 + u < H) {
-        rq[u] = *reinterpret_cast<const uint4 *>(q + (h0 + u) * head_stride + row_off);
-        rk[u] = *reinterpret_cast<const uint4 *>(k + (h0 + u) * head_stride + row_off);
+        rq[u] = load_stream(q + (h0 + u) * head_stride + row_off);
+        rk[u] = load_stream(k + (h0 + u) * head_stride + row_off);
       }
     }
 #pragma unroll
     for (int u = 0; u < kHeadUnroll; ++u) {
       if (h0 + u < H) {
-        *reinterpret_cast<uint4 *>(q + (h0 + u) * head_stride + row_off) = norm_rope8(rq[u], gq, c, s, eps);
-        *reinterpret_cast<uint4 *>(k + (h0 + u) * head_stride + row_off) = norm_rope8(rk[u], gk, c, s, eps);
+        store_stream(q + (h0 + u) * head_stride + row_off, norm_rope8(rq[u], gq, c, s, eps));
+        store_stream(k + (h0 + u) * head_stride + row_off, norm_rope8(rk[u], gk, c, s, eps));
       }
     }
   }
