@@ -78,8 +78,10 @@ def summarize(args):
         out.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
         for r in rows:
             name = _kernel_short(r["Name"])
-            if "FillFunctor" in r["Name"]:
-                name = "torch fill (cache flush)"
+            if "reduce_kernel" in r["Name"]:
+                name = "torch amax (read-only cache flush)"
+            elif "FillFunctor" in r["Name"] or "fillBuffer" in r["Name"]:
+                name = "torch fill"
             elif "copyBuffer" in r["Name"]:
                 name = "device copies (largest = 512 MiB calibration)"
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
@@ -89,8 +91,9 @@ def summarize(args):
         for d in args.pmc:
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
-                    key = ("attn" if "attn_fwd_kernel" in r["Kernel_Name"] else
-                           "copy" if "copy" in r["Kernel_Name"].lower() else None)
+                    key = ("attn" if "attn_fwd_kernel<false>" in r["Kernel_Name"] or
+                           r["Kernel_Name"].startswith("h3::(anonymous namespace)::attn_fwd_kernel(") else
+                           "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
                         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
         out.append(f"# rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), workload {args.workload}")
@@ -121,14 +124,14 @@ def prologue_bytes(H, L, D=128):
 def cpu_baseline(x, w, budget_s=20.0):
     """The oracle on a bounded sample of the same workload, timed on the host:
     for heads 0, 1, ... until the budget is spent: the prologue of that head's k
-    (all L rows) and of the 4096 parity-sample q rows, then attention for those rows."""
+    (all L rows) and of 16384 seeded sample q rows, then attention for those rows."""
     import torch
     import oracle
     from exact_head_attention_amd import inputs as I
     cores = torch.get_num_threads()
     rows_done, heads, t_total = 0, 0, 0.0
     c_ref, s_ref = oracle.rope_tables(x["positions"], w.D, x["theta"])
-    n_rows = 4096
+    n_rows = 16384
     for h in range(w.H):
         rows = I.sample_rows(w, h, n_rows)
         t0 = time.perf_counter()
@@ -227,12 +230,12 @@ def main():
     att_ms = float(np.mean(att_ms_all))
 
     # Prologue alone with the 256 MB last-level cache flushed before each
-    # launch.  The flush only reads (a sum over 512 MiB), so no dirty lines
-    # are still being written back while the timed launch runs.
-    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    # launch.  The flush only reads (one max-reduction over 512 MiB), so no
+    # dirty lines are still being written back while the timed launch runs.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     pro_cold = []
     for _ in range(20):
-        flush.sum(dtype=torch.int32)
+        flush.amax()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         B.qknorm_rope(q, k, gq, gk, cos, sin, x["eps"])
