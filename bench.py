@@ -76,8 +76,11 @@ def summarize(args):
         out.append(f"# command: {args.command}")
         out.append(f"# attn_fwd.hip sha256[:16] = {source_digest()}")
         out.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+        call_us = 0.0
         for r in rows:
             name = _kernel_short(r["Name"])
+            if name.startswith("attn_fwd_kernel<") and name.endswith("false>"):
+                call_us += float(r["AverageNs"]) / 1e3
             if "reduce_kernel" in r["Name"]:
                 name = "torch amax (read-only cache flush)"
             elif "FillFunctor" in r["Name"] or "fillBuffer" in r["Name"]:
@@ -86,13 +89,15 @@ def summarize(args):
                 name = "device copies (largest = 512 MiB calibration)"
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+        out.append(f"# one h3_attention call = attn_fwd_kernel<8, false> (full rounds) + attn_fwd_kernel<4, false> "
+                   f"(tail, when launched): {call_us:.2f} us per call")
     if args.pmc:
         per = {}
         for d in args.pmc:
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
-                    key = ("attn" if "attn_fwd_kernel<false>" in r["Kernel_Name"] or
-                           r["Kernel_Name"].startswith("h3::(anonymous namespace)::attn_fwd_kernel(") else
+                    key = ("attn_main" if "attn_fwd_kernel<8, false>" in r["Kernel_Name"] else
+                           "attn_tail" if "attn_fwd_kernel<4, false>" in r["Kernel_Name"] else
                            "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
                         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
@@ -108,6 +113,10 @@ def summarize(args):
             val = max(vals) if key == "copy" else sum(vals) / len(vals)
             out.append(f"{key}_{short}: {val:.1f}")
             out.append(f"# {key} {cname}: {len(vals)} dispatches, min {min(vals):.1f}, max {max(vals):.1f}")
+        # One h3_attention call is the main launch plus the tail launch (if any).
+        for cname, short in (("FETCH_SIZE", "fetch_kib"), ("WRITE_SIZE", "write_kib")):
+            tot = sum(sum(v) / len(v) for (key, c), v in per.items() if key.startswith("attn_") and c == cname)
+            out.append(f"attn_{short}: {tot:.1f}")
     print("\n".join(out))
 
 
@@ -274,7 +283,7 @@ def main():
                                f"({w.n_video} video + {w.n_audio} audio tokens), D={w.D}",
                    "H": w.H, "L": w.L, "D": w.D, "seed": args.seed},
         "pct_of_bf16_peak": round(100 * value / BF16_MFMA_PEAK_TFLOPS, 2),
-        "roofline": {"kernel": "attn_fwd_kernel", "bound": "mfma", "achieved": round(att_tflops, 2),
+        "roofline": {"kernel": "h3_attention (attn_fwd_kernel: full-round launch + tail launch)", "bound": "mfma", "achieved": round(att_tflops, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": read_counter_summary(w.name),
                      "avg_launch_ms": round(att_ms, 4), "min_launch_ms": round(min(att_ms_all), 4),

@@ -6,7 +6,9 @@
 // no mask, any length).  Flash-style: the L x L scores never leave registers.
 //
 // Work decomposition
-//   * One workgroup = one (head, 256-query tile); 8 waves, 32 query rows each.
+//   * Work unit = one (head, 256-query tile); each wave owns 32 query rows.
+//     A unit runs as one 8-wave workgroup, or, in the tail launch, as two
+//     4-wave workgroups of 128 rows each (see launch_split below).
 //   * Keys stream in tiles of 64 through double-buffered LDS: K row-major
 //     [key][d], V transposed [d][key] (the transpose happens on the way in).
 //   * Per wave and key tile, with v_mfma_f32_32x32x16_bf16:
@@ -23,10 +25,12 @@
 //   * Softmax works in base 2: p = 2^(s * scale*log2(e) - m), the same value
 //     as e^(scale*s - m') with m' = m / log2(e).
 //
-// Determinism: a workgroup's arithmetic depends only on its (head, q-tile)
-// and keys are visited in a fixed order, so every head's output is bit-
-// identical however many heads one launch covers.  The XCD-aware block remap
-// changes only where a tile runs.
+// Determinism: a row's arithmetic depends only on its (head, row) and keys
+// are visited in a fixed order; 8- and 4-wave workgroups run the same per-wave
+// code and differ only in how many LDS staging chunks each thread carries.  So
+// every head's output is bit-identical however many heads one launch covers.
+// The XCD-aware block remap and the main/tail split change only where and
+// when a row runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,9 +47,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = kHeadDim;
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBr = kWaves * 32;     // query rows per workgroup
+constexpr int kUnitRows = 256;       // query rows per work unit (8 waves x 32)
 constexpr int kBc = 64;              // keys per tile
 constexpr int kKStride = D + 8;      // bf16 per K row in LDS (272 B: rows shift 4 banks)
 constexpr int kVStride = D + 32;     // bf16 per V row in LDS (320 B: transpose reads hit 4 disjoint bank windows)
@@ -74,9 +76,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 __device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 // Maps the hardware's round-robin placement of blocks over the 8 XCDs onto
@@ -116,11 +115,18 @@ __device__ __forceinline__ float max32(const f32x16 &a, const f32x16 &b) {
 // natural log of sum_j exp(scale q.k_j) over the Lk keys given (the partial
 // form h3_attention_merge combines).  Queries: [H][Lq][D]; keys and values:
 // element (h, j, d) at h*kv_stride + j*D + d, j < Lk.
-template <bool kLse>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
+//
+// NW waves per workgroup (8: one whole unit; 4: half a unit).  Block b covers
+// unit unit_base + r / (8/NW), part r % (8/NW), with r the XCD-remapped b.
+template <int NW, bool kLse>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
-    long long kv_stride, int n_qtiles, float scale_log2e) {
+    long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kParts = 8 / NW;           // workgroups per unit
+  constexpr int kChunks = 16 / NW;         // 16-byte staging chunks per thread per tensor and tile
+  static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBc * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBc * kVStride];
 
@@ -129,8 +135,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int l32 = lane & 31, g = lane >> 5;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int head = logical / n_qtiles;
-  const int qt = logical - head * n_qtiles;
+  const int unit = unit_base + logical / kParts;
+  const int head = unit / n_qtiles;
+  const int qt = unit - head * n_qtiles;
+  const int row0 = qt * kUnitRows + (logical % kParts) * (NW * 32);
+  if (row0 >= Lq) return;   // the empty half of a ragged last unit (uniform per block)
   const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Qh = Q + head_off;
   const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
@@ -138,26 +147,32 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int row_bytes = D * 2;
 
   // Q^T fragments (B operand): lane holds query row qrow, d = 16c + 8g .. +7.
-  const int qrow = qt * kBr + wave * 32 + l32;
+  const int qrow = row0 + wave * 32 + l32;
   bf16x8 qf[8];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, Lq * row_bytes);
+    // Descriptor over this workgroup's rows only: sizes stay below 2^31 bytes
+    // for any L the API accepts.
+    const int rows_left = Lq - row0 < NW * 32 ? Lq - row0 : NW * 32;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + static_cast<size_t>(row0) * D, rows_left * row_bytes);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, qrow * row_bytes + 32 * c + 16 * g));
+      qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, (wave * 32 + l32) * row_bytes + 32 * c + 16 * g));
   }
 
   // Staging of one key tile: 64 rows x 16 chunks of 16 B for each of K and
-  // V; thread takes chunks tid and tid + 512 (tile-relative byte offset
-  // chunk * 16).  Both land row-major in LDS.
-  auto load_kv = [&](const uint16_t *base, int kt, uint4 (&r)[2]) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (Lk - kt * kBc) * row_bytes);
-    r[0] = bload128(rs, tid * 16);
-    r[1] = bload128(rs, (tid + kThreads) * 16);
-  };
-  auto store_rows = [&](uint16_t *dst, int stride, const uint4 (&r)[2]) {
+  // V; thread takes chunks tid + i * kThreads, i < kChunks (tile-relative
+  // byte offset chunk * 16).  Both land row-major in LDS.
+  using Chunks = uint4[kChunks];
+  auto load_kv = [&](const uint16_t *base, int kt, Chunks &r) {
+    const int keys_left = Lk - kt * kBc;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (keys_left < kBc ? keys_left : kBc) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kChunks; ++i) r[i] = bload128(rs, (tid + kThreads * i) * 16);
+  };
+  auto store_rows = [&](uint16_t *dst, int stride, const Chunks &r) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
       const int c = tid + kThreads * i;
       *reinterpret_cast<uint4 *>(dst + (c >> 4) * stride + (c & 15) * 8) = r[i];
     }
@@ -188,15 +203,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   const int n_kt = (Lk + kBc - 1) / kBc;
   // Staging registers, two sets: a step stores the set loaded one step
   // earlier and refills the other, so global-load latency hides behind a
-  // whole step.  Set layout: [0..1] K chunks, [2..3] V chunks.
-  uint4 stage0[4], stage1[4];
+  // whole step.  Set layout: [0, kChunks) K chunks, [kChunks, 2 kChunks) V.
+  uint4 stage0[2 * kChunks], stage1[2 * kChunks];
+  auto kpart = [](uint4 *st) -> Chunks & { return *reinterpret_cast<Chunks *>(st); };
+  auto vpart = [](uint4 *st) -> Chunks & { return *reinterpret_cast<Chunks *>(st + kChunks); };
   {
-    uint4 k0[2], v0[2], k1[2];
+    uint4 k0[kChunks], v0[kChunks], k1[kChunks];
     load_kv(Kh, 0, k0);
     load_kv(Vh, 0, v0);
     load_kv(Kh, 1, k1);
-    load_kv(Kh, 2, *reinterpret_cast<uint4(*)[2]>(&stage0[0]));
-    load_kv(Vh, 1, *reinterpret_cast<uint4(*)[2]>(&stage0[2]));
+    load_kv(Kh, 2, kpart(stage0));
+    load_kv(Vh, 1, vpart(stage0));
     store_rows(k_lds[0], kKStride, k0);
     store_rows(v_lds[0], kVStride, v0);
     store_rows(k_lds[1], kKStride, k1);
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
   // One key tile: softmax of s_cur (tile kt), scores of tile kt+1 into s_nxt,
   // O += P.V for tile kt, then LDS staging of K tile kt+2 and V tile kt+1
   // from st_store while st_load fetches K tile kt+3 and V tile kt+2.
-  auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 (&st_store)[4], uint4 (&st_load)[4]) {
+  auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 *st_store, uint4 *st_load) {
     // (1) Mask the ragged tail, row max, and (rarely) raise the running max.
     // s_cur[b][i] holds key kt*64 + 32b + 16(i/8) + 8g + i%8.
     const int key_base = kt * kBc;
@@ -258,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
     }
     const float neg_m = -m_run;
 
-    load_kv(Kh, kt + 3, *reinterpret_cast<uint4(*)[2]>(&st_load[0]));
-    load_kv(Vh, kt + 2, *reinterpret_cast<uint4(*)[2]>(&st_load[2]));
+    load_kv(Kh, kt + 3, kpart(st_load));
+    load_kv(Vh, kt + 2, vpart(st_load));
 
     // (2) Scores of tile kt+1 on the matrix cores, interleaved step by step
     // with the exponentials of tile kt on the vector ALUs; K fragments are
@@ -321,8 +338,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);     // 4 MFMAs
     }
-    store_rows(k_lds[kt & 1], kKStride, *reinterpret_cast<uint4(*)[2]>(&st_store[0]));
-    store_rows(v_lds[(kt + 1) & 1], kVStride, *reinterpret_cast<uint4(*)[2]>(&st_store[2]));
+    store_rows(k_lds[kt & 1], kKStride, kpart(st_store));
+    store_rows(v_lds[(kt + 1) & 1], kVStride, vpart(st_store));
     __syncthreads();
   };
 
@@ -368,25 +385,55 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(
 }  // namespace
 
 int64_t attention_grid(int H, int L) {
-  return static_cast<int64_t>(H) * ((static_cast<int64_t>(L) + kBr - 1) / kBr);
+  return static_cast<int64_t>(H) * ((static_cast<int64_t>(L) + kUnitRows - 1) / kUnitRows);
 }
+
+namespace {
+
+// Main launch + tail launch.  Units run in rounds of one 8-wave workgroup per
+// CU; when the last round would leave at least half the CUs idle (r <= CUs/2
+// units left over), those r units instead run as 2r 4-wave workgroups, one
+// per CU, after the full rounds (the same stream orders the two launches).
+// A 4-wave workgroup has one wave per SIMD to itself, so the tail round takes
+// well under a full round's time.  Which launch a unit lands in depends on H
+// and on the device, but a row's arithmetic does not.
+template <bool kLse>
+hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, float *out32,
+                        float *lse, int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
+  const int n_qtiles = (Lq + kUnitRows - 1) / kUnitRows;
+  const int units = static_cast<int>(attention_grid(H, Lq));
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int rem = cus > 0 ? units % cus : 0;
+  const int tail = (cus > 0 && rem <= cus / 2) ? rem : 0;
+  const int main_units = units - tail;
+  const float sl2e = scale * kLog2e;
+  if (main_units > 0) {
+    hipLaunchKernelGGL((attn_fwd_kernel<8, kLse>), dim3(main_units), dim3(512), 0, stream, q, k, v, out, out32,
+                       lse, Lq, Lk, kv_stride, n_qtiles, 0, sl2e);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (tail > 0) {
+    hipLaunchKernelGGL((attn_fwd_kernel<4, kLse>), dim3(2 * tail), dim3(256), 0, stream, q, k, v, out, out32,
+                       lse, Lq, Lk, kv_stride, n_qtiles, main_units, sl2e);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, int H,
                             int L, float scale, hipStream_t stream) {
-  const int n_qtiles = (L + kBr - 1) / kBr;
-  const int blocks = static_cast<int>(attention_grid(H, L));
-  hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v, out, nullptr,
-                     nullptr, L, L, static_cast<long long>(L) * D, n_qtiles, scale * kLog2e);
-  return hipGetLastError();
+  return launch_split<false>(q, k, v, out, nullptr, nullptr, H, L, L, static_cast<long long>(L) * D, scale,
+                             stream);
 }
 
 hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
                                 int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
-  const int n_qtiles = (Lq + kBr - 1) / kBr;
-  const int blocks = static_cast<int>(attention_grid(H, Lq));
-  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, q, k, v, nullptr, out, lse,
-                     Lq, Lk, kv_stride, n_qtiles, scale * kLog2e);
-  return hipGetLastError();
+  return launch_split<true>(q, k, v, nullptr, out, lse, H, Lq, Lk, kv_stride, scale, stream);
 }
 
 // Merge of P partial results: one 32-lane half-wave per (head, row); lane

@@ -17,7 +17,7 @@ hipError_t launch_rope_tables(const int *positions, int L, int half,
                               double theta, float *cos_t, float *sin_t,
                               hipStream_t stream);
 
-// Number of workgroups h3_attention launches for H heads of L tokens.
+// Number of 256-row work units (head, query tile) for H heads of L tokens.
 int64_t attention_grid(int H, int L);
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k,

@@ -17,6 +17,10 @@ self-attention):
   ws2          H=28, L=32768,  same layout
   ws1          H=56, L=32768,  same layout
   canvas128k   H=7,  L=131072, 126976 video + 4096 audio; q and k drawn x3
+  odd37726     H=7,  L=37726,  a real-length sequence that is not a multiple of
+               any tile (the 768p canvas with a short prompt, whn09's Neuron
+               FYI); split read as 32256 video (32 latent frames of 42x24
+               patches) + 5470 audio
 
 Draw order from numpy.random.Generator(PCG64(seed)): q, k, v (standard normal,
 fp32, times the workload's qk_scale for q and k), then gamma_q and gamma_k
@@ -61,6 +65,7 @@ WORKLOADS = {
     "ws1": Workload("ws1", H=56, L=32768, n_video=31744, n_audio=1024),
     "canvas128k": Workload("canvas128k", H=7, L=131072, n_video=126976,
                            n_audio=4096, qk_scale=3.0),
+    "odd37726": Workload("odd37726", H=7, L=37726, n_video=32256, n_audio=5470),
 }
 
 

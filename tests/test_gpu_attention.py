@@ -91,6 +91,26 @@ def test_attention_special_cases(gpu_lib):
     assert err.max() <= ATTN_TOL, err.max()
 
 
+@pytest.mark.parametrize("L", [4900, 5000])
+def test_attention_tail_workgroups_bit_identical(gpu_lib, L):
+    """Ten heads in one launch (200 units of 256 rows: with 256 CUs all run as
+    8-wave workgroups) against one launch per head (20 units: all run as the
+    4-wave half-unit workgroups of the tail launch, the second half of the
+    last unit empty at L = 4900): every head bit-identical, and the full
+    launch within the bar of the oracle on sampled rows."""
+    import torch
+    q, k, v = _raw(10, L, seed=40 + L)
+    w = I.custom_workload(H=10, L=L)
+    rows = [I.sample_rows(w, h, 256) for h in range(10)]
+    full = _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), rows, label=f"10 heads L={L}")
+    single = torch.empty_like(full)
+    for h in range(10):
+        gpu_lib.attention(q[h:h + 1], k[h:h + 1], v[h:h + 1], out=single[h:h + 1])
+    torch.cuda.synchronize()
+    for h in range(10):
+        assert torch.equal(single[h], full[h]), f"head {h} differs between the launches"
+
+
 def test_attention_peaky_logits(gpu_lib):
     """Large logits (q, k ~ 3 N(0,1) at scale 1/sqrt(128): logit sd ~ 9) stress
     the running max and the rescaling of the accumulator."""
@@ -112,6 +132,13 @@ def _sampled_workload(gpu_lib, name, with_prologue=True):
 
 def test_attention_ws8_sampled(gpu_lib):
     _sampled_workload(gpu_lib, "ws8")
+
+
+def test_attention_odd37726_sampled(gpu_lib):
+    """A real odd length (37726 = not a multiple of any tile): prologue, then
+    attention, 4096 sampled rows per head (segment boundaries and the last
+    row included)."""
+    _sampled_workload(gpu_lib, "odd37726")
 
 
 @pytest.mark.timeout(600)

@@ -17,6 +17,7 @@ def test_workload_shapes_match_the_rank_shares():
     for w in I.WORKLOADS.values():
         assert w.n_video + w.n_audio == w.L and w.D == 128
     assert I.WORKLOADS["canvas128k"].qk_scale == 3.0
+    assert I.WORKLOADS["odd37726"].L == 37726 and 37726 % 64 != 0
 
 
 def test_make_inputs_deterministic_and_distributed():
