@@ -160,6 +160,65 @@ def cpu_baseline(x, w, budget_s=20.0):
                       f"({t_total:.1f} s)"}
 
 
+def bench_projection(args):
+    """The rank's qkv projection with the fused QK-norm + RoPE epilogue
+    (h3_qkv_proj_qknorm_rope) on a projection workload: one JSON line."""
+    import torch
+    from exact_head_attention_amd import binding as B
+    from exact_head_attention_amd import inputs as I
+
+    w = I.PROJ_WORKLOADS[args.workload]
+    log(f"bench: projection {w.name} H={w.H} L={w.L} hidden={w.hidden}; generating inputs")
+    x = I.make_proj_inputs(w, args.seed)
+    dev = torch.device("cuda:0")
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).view(dt).to(dev)
+
+    xs, wq, wk, wv = (up(x[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv"))
+    gq, gk = up(x["gamma_q"], torch.float32), up(x["gamma_k"], torch.float32)
+    cos, sin = B.rope_tables(up(x["positions"], torch.int32), w.D, x["theta"])
+    outs = tuple(torch.empty((w.H, w.L, w.D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    stream = torch.cuda.current_stream()
+
+    def call():
+        B.qkv_proj_qknorm_rope(xs, wq, wk, wv, gq, gk, cos, sin, x["eps"], out=outs)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_all = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.mean(ms_all))
+    tflops = w.flops / (ms / 1e3) / 1e12
+    # HBM bytes the call must move: x and the weight slices read once, q, k, v
+    # written once, tables and gammas read once.
+    bytes_alg = 2 * w.L * w.hidden + 3 * 2 * w.H * w.D * w.hidden + 3 * 2 * w.H * w.L * w.D + 2 * 4 * w.L * 64
+    rec = {
+        "metric": "qkv projection TFLOPS (2*L*3*H*D*hidden per call, QK-norm + RoPE fused) and % bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden state, N(0,1/hidden) weights)",
+        "config": {"workload": f"{w.name}: row-sliced qkv_proj of H={w.H} heads over L={w.L} tokens, "
+                               f"hidden={w.hidden}, D={w.D}", "H": w.H, "L": w.L, "hidden": w.hidden,
+                   "seed": args.seed},
+        "roofline": {"kernel": "qkv_proj_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 4), "min_launch_ms": round(min(ms_all), 4),
+                     "flops_per_launch": w.flops, "algorithmic_bytes": bytes_alg},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,9 +244,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from exact_head_attention_amd import inputs as I
+    if args.workload in I.PROJ_WORKLOADS:
+        bench_projection(args)
+        return
+
     import torch
     from exact_head_attention_amd import binding as B
-    from exact_head_attention_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
     log(f"bench: workload {w.name} H={w.H} L={w.L} D={w.D}; generating inputs")

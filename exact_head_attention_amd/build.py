@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libh3attn.so")
 
-SOURCES = ["h3attn_api.cpp", "qknorm_rope.hip", "attn_fwd.hip"]
+SOURCES = ["h3attn_api.cpp", "qknorm_rope.hip", "attn_fwd.hip", "qkv_proj.hip"]
 
 # Per-source device flags.  The attention kernel assumes finite inputs (the
 # ABI documents it), so the NaN-quieting that max() otherwise needs is

@@ -38,7 +38,7 @@ const char *h3_status_string(int status) {
   switch (status) {
     case H3_OK: return "ok";
     case H3_ERR_NULL: return "a required pointer is NULL";
-    case H3_ERR_SHAPE: return "H and L must be >= 1 and H*L < 2^31";
+    case H3_ERR_SHAPE: return "a size is out of range (H, L >= 1, H*L < 2^31, hidden a multiple of 32)";
     case H3_ERR_UNSUPPORTED: return "only head_dim D == 128 is supported";
     case H3_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case H3_ERR_ALIAS: return "output and input buffers overlap";
@@ -152,6 +152,41 @@ int h3_rope_tables(const int *positions, int L, int D, double theta,
   if (static_cast<int64_t>(L) * (D / 2) >= (int64_t{1} << 31)) return H3_ERR_SHAPE;
   hipError_t e = h3::launch_rope_tables(positions, L, D / 2, theta, cos, sin,
                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const void *wv,
+                            const float *gamma_q, const float *gamma_k, const float *cos,
+                            const float *sin, void *q, void *k, void *v, int H, int L,
+                            int hidden, int D, float eps, void *stream) {
+  if (!x || !wq || !wk || !wv || !gamma_q || !gamma_k || !cos || !sin || !q || !k || !v) return H3_ERR_NULL;
+  if (!shape_ok(H, L) || hidden < 32 || hidden % 32 != 0 || hidden > (1 << 20) ||
+      h3::qkv_proj_grid(H, L) >= (int64_t{1} << 31))
+    return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  const void *ptrs[] = {x, wq, wk, wv, gamma_q, gamma_k, cos, sin, q, k, v};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return H3_ERR_ALIGN;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return H3_ERR_VALUE;
+  const uint64_t x_bytes = static_cast<uint64_t>(L) * hidden * 2;
+  const uint64_t w_bytes = static_cast<uint64_t>(H) * D * hidden * 2;
+  const uint64_t t_bytes = static_cast<uint64_t>(H) * L * D * 2;
+  const uint64_t tab_bytes = static_cast<uint64_t>(L) * (D / 2) * 4;
+  const void *outs[] = {q, k, v};
+  const struct { const void *p; uint64_t n; } ins[] = {
+      {x, x_bytes}, {wq, w_bytes}, {wk, w_bytes}, {wv, w_bytes}, {gamma_q, D * 4u},
+      {gamma_k, D * 4u}, {cos, tab_bytes}, {sin, tab_bytes}};
+  for (int i = 0; i < 3; ++i) {
+    for (const auto &in : ins)
+      if (overlaps(outs[i], t_bytes, in.p, in.n)) return H3_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], t_bytes, outs[j], t_bytes)) return H3_ERR_ALIAS;
+  }
+  hipError_t e = h3::launch_qkv_proj_qknorm_rope(
+      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wq), static_cast<const uint16_t *>(wk),
+      static_cast<const uint16_t *>(wv), gamma_q, gamma_k, cos, sin, static_cast<uint16_t *>(q),
+      static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 

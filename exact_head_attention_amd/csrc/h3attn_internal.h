@@ -30,4 +30,12 @@ hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint
 hipError_t launch_attention_merge(const float *outs, const float *lses, int P, uint16_t *out, float *lse_out,
                                   int H, int L, hipStream_t stream);
 
+// Number of workgroups h3_qkv_proj_qknorm_rope launches.
+int64_t qkv_proj_grid(int H, int L);
+
+hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, const uint16_t *wk,
+                                       const uint16_t *wv, const float *gamma_q, const float *gamma_k,
+                                       const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k,
+                                       uint16_t *v, int H, int L, int C, float eps, hipStream_t stream);
+
 }  // namespace h3

@@ -1,0 +1,239 @@
+// Row-sliced qkv projection with QK-RMSNorm + RoPE in the epilogue, for gfx950.
+//
+// A rank that holds the whole (gathered) hidden state x [L][C] projects it
+// through only its own heads' rows of qkv_proj: wq, wk, wv are [H*128][C]
+// ("buqi-minimax-h3-multigpu", How it works: the all_gather form for small
+// world sizes, where slicing rows of the weight is exact).  q and k then get
+// the head_dim RMSNorm and the rotary embedding ("Tensor parallelism for
+// MiniMax-H3", PR description), fused here into the GEMM epilogue so the
+// projection never goes through HBM in between and is never rounded before
+// the norm.  Outputs are [H][L][128] bf16, the layout the attention reads.
+//
+// Work decomposition
+//   * Workgroup = (feature tile, token tile): 128 output features (one head
+//     of q, k or v) x 256 tokens; 4 waves, each 128 features x 64 tokens.
+//   * The product is computed transposed, C^T = W . X^T, with
+//     v_mfma_f32_32x32x16_bf16: A = weight rows (features), B = hidden rows
+//     (tokens).  Both operands are K-contiguous in memory, so every fragment
+//     is one 16-byte LDS read.  The accumulator puts one token per lane
+//     column and 16 features per lane, so a token's sum of squares over its
+//     128 features is lane-local plus one lane-half exchange, and each RoPE
+//     pair (2j, 2j+1) sits in one lane.
+//   * The hidden dimension streams in steps of 32 through double-buffered LDS
+//     (80-byte padded rows: 8 consecutive rows hit 8 disjoint bank groups);
+//     global loads are buffer loads one step ahead, so the last partial token
+//     tile reads zeros and writes nothing past L.
+//   * Blocks are ordered so that the 64 workgroups an XCD runs at once cover
+//     8 token tiles x 8 feature tiles: each hidden-state tile and each weight
+//     tile is then read by 8 concurrent workgroups through that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "h3attn_internal.h"
+
+namespace h3 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = kHeadDim;          // features per head = per feature tile
+constexpr int kTok = 256;            // tokens per workgroup
+constexpr int kThreads = 256;        // 4 waves
+constexpr int kK = 32;               // hidden elements per LDS step
+constexpr int kStride = kK + 8;      // bf16 per LDS row (80 B)
+constexpr int kWChunks = D * (kK / 8) / kThreads;     // 16-byte chunks per thread per step: 2
+constexpr int kXChunks = kTok * (kK / 8) / kThreads;  // 4
+constexpr int kGroupTiles = 8;       // token tiles per placement group
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
+}
+__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float lane_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// Contiguous logical ranges per XCD (the hardware deals blocks round-robin).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = nblk >> 3, extra = nblk & 7;
+  return xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wq, const uint16_t *__restrict__ Wk,
+    const uint16_t *__restrict__ Wv, const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
+    const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
+    uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][D * kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t x_lds[2][kTok * kStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // logical -> (token group, feature tile, token tile within the group)
+  const int n_ft = 3 * H;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = kGroupTiles * n_ft;
+  const int tg = logical / per_group;
+  const int rem = logical - tg * per_group;
+  const int gsz = min(kGroupTiles, n_ttiles - tg * kGroupTiles);
+  const int ft = rem / gsz;
+  const int tt = tg * kGroupTiles + (rem - ft * gsz);
+  const int which = ft / H;          // 0 q, 1 k, 2 v
+  const int head = ft - which * H;
+  const int t0 = tt * kTok;
+
+  const uint16_t *Wsel = which == 0 ? Wq : which == 1 ? Wk : Wv;
+  const int row_bytes = C * 2;
+  const int tok_rows = L - t0 < kTok ? L - t0 : kTok;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wsel + static_cast<size_t>(head) * D * C, D * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * C, tok_rows * row_bytes);
+
+  // Staging: chunk c = tid + 256 i of a step covers row c/4, bytes 16 (c%4)
+  // of the step's 64-byte slice of that row.
+  uint4 sw[kWChunks], sx[kXChunks];
+  auto load = [&](int ks) {
+    const uint32_t kb = static_cast<uint32_t>(ks) * kK * 2;
+#pragma unroll
+    for (int i = 0; i < kWChunks; ++i) {
+      const int c = tid + kThreads * i;
+      sw[i] = bload128(rw, (c >> 2) * row_bytes + kb + 16 * (c & 3));
+    }
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      const int c = tid + kThreads * i;
+      sx[i] = bload128(rx, (c >> 2) * row_bytes + kb + 16 * (c & 3));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kWChunks; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4 *>(&w_lds[buf][(c >> 2) * kStride + 8 * (c & 3)]) = sw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4 *>(&x_lds[buf][(c >> 2) * kStride + 8 * (c & 3)]) = sx[i];
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) acc[fs][ts] = f32x16{};
+
+  const int n_k = C / kK;
+  load(0);
+  store(0);
+  if (n_k > 1) load(1);
+  __syncthreads();
+
+  // Fragment addresses: A = weight row 32fs + l32, B = token row 64w + 32ts + l32,
+  // both at hidden offset 16kk + 8g within the step.
+  const uint16_t *wa = &w_lds[0][l32 * kStride + 8 * g];
+  const uint16_t *xb = &x_lds[0][(wave * 64 + l32) * kStride + 8 * g];
+  for (int ks = 0; ks < n_k; ++ks) {
+    const int buf = ks & 1;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 a[4], b[2];
+#pragma unroll
+      for (int fs = 0; fs < 4; ++fs)
+        a[fs] = *reinterpret_cast<const bf16x8 *>(wa + buf * (D * kStride) + fs * 32 * kStride + 16 * kk);
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+        b[ts] = *reinterpret_cast<const bf16x8 *>(xb + buf * (kTok * kStride) + ts * 32 * kStride + 16 * kk);
+#pragma unroll
+      for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+          acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
+    }
+    if (ks + 1 < n_k) {
+      // Buffer buf^1 was last read in step ks-1, before the barrier that
+      // ended it; step ks+2's loads refill the staging registers.
+      store(buf ^ 1);
+      if (ks + 2 < n_k) load(ks + 2);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[fs][ts][i] = feature 32fs + 8(i/4) + 4g + i%4 of token
+  // t0 + 64w + 32ts + l32.
+  uint16_t *Out = which == 0 ? Qo : which == 1 ? Ko : Vo;
+  const float *gamma = which == 0 ? gamma_q : gamma_k;
+#pragma unroll
+  for (int ts = 0; ts < 2; ++ts) {
+    const int t = t0 + wave * 64 + ts * 32 + l32;
+    float r = 1.0f;
+    if (which < 2) {
+      float ss = 0.f;
+#pragma unroll
+      for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(acc[fs][ts][i], acc[fs][ts][i], ss);
+      ss = lane_half_sum(ss);
+      r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+    }
+    if (t >= L) continue;
+    uint16_t *orow = Out + (static_cast<size_t>(head) * L + t) * D;
+#pragma unroll
+    for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int f0 = 32 * fs + 8 * q4 + 4 * g;   // 4 consecutive features f0 .. f0+3
+        const float e[4] = {acc[fs][ts][4 * q4], acc[fs][ts][4 * q4 + 1], acc[fs][ts][4 * q4 + 2],
+                            acc[fs][ts][4 * q4 + 3]};
+        uint2 w;
+        if (which < 2) {
+          const float4 gm = *reinterpret_cast<const float4 *>(gamma + f0);
+          const float2 c = *reinterpret_cast<const float2 *>(cos_t + static_cast<size_t>(t) * (D / 2) + f0 / 2);
+          const float2 s = *reinterpret_cast<const float2 *>(sin_t + static_cast<size_t>(t) * (D / 2) + f0 / 2);
+          const float y0 = e[0] * r * gm.x, y1 = e[1] * r * gm.y;
+          const float y2 = e[2] * r * gm.z, y3 = e[3] * r * gm.w;
+          w.x = pack_bf16x2(y0 * c.x - y1 * s.x, y0 * s.x + y1 * c.x);
+          w.y = pack_bf16x2(y2 * c.y - y3 * s.y, y2 * s.y + y3 * c.y);
+        } else {
+          w.x = pack_bf16x2(e[0], e[1]);
+          w.y = pack_bf16x2(e[2], e[3]);
+        }
+        *reinterpret_cast<uint2 *>(orow + f0) = w;
+      }
+  }
+}
+
+}  // namespace
+
+int64_t qkv_proj_grid(int H, int L) {
+  return static_cast<int64_t>(3) * H * ((static_cast<int64_t>(L) + kTok - 1) / kTok);
+}
+
+hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, const uint16_t *wk,
+                                       const uint16_t *wv, const float *gamma_q, const float *gamma_k,
+                                       const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k,
+                                       uint16_t *v, int H, int L, int C, float eps, hipStream_t stream) {
+  const int n_ttiles = (L + kTok - 1) / kTok;
+  const int blocks = static_cast<int>(qkv_proj_grid(H, L));
+  hipLaunchKernelGGL(qkv_proj_kernel, dim3(blocks), dim3(kThreads), 0, stream, x, wq, wk, wv, gamma_q, gamma_k,
+                     cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -25,6 +25,17 @@ self-attention):
 Draw order from numpy.random.Generator(PCG64(seed)): q, k, v (standard normal,
 fp32, times the workload's qk_scale for q and k), then gamma_q and gamma_k
 (1 + 0.1 * standard normal, fp32).
+
+Projection workloads (the rank's row-sliced qkv_proj over the gathered hidden
+state, H3's hidden size 5376; "buqi-minimax-h3-multigpu", How it works):
+
+  proj_tiny    H=2,  L=300,   hidden=512   (256 video + 44 audio)
+  proj_ws8     H=7,  L=32768, hidden=5376  (31744 video + 1024 audio)
+  proj_ws2     H=28, L=32768, hidden=5376  (the all_gather form's world_size 2)
+
+Draw order from Generator(PCG64(seed)): x (standard normal), then wq, wk, wv
+(standard normal / sqrt(hidden), so each projected feature is about N(0,1)),
+each rounded to bf16; then gamma_q and gamma_k (1 + 0.1 * standard normal).
 """
 from __future__ import annotations
 
@@ -67,6 +78,47 @@ WORKLOADS = {
                            n_audio=4096, qk_scale=3.0),
     "odd37726": Workload("odd37726", H=7, L=37726, n_video=32256, n_audio=5470),
 }
+
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    name: str
+    H: int
+    L: int
+    n_video: int
+    n_audio: int
+    hidden: int
+    D: int = HEAD_DIM
+
+    @property
+    def flops(self) -> float:
+        """2 * L * (3 H D) * hidden: one multiply-add per token, feature and
+        hidden element."""
+        return 2.0 * self.L * 3 * self.H * self.D * self.hidden
+
+
+PROJ_WORKLOADS = {
+    "proj_tiny": ProjWorkload("proj_tiny", H=2, L=300, n_video=256, n_audio=44, hidden=512),
+    "proj_ws8": ProjWorkload("proj_ws8", H=7, L=32768, n_video=31744, n_audio=1024, hidden=5376),
+    "proj_ws2": ProjWorkload("proj_ws2", H=28, L=32768, n_video=31744, n_audio=1024, hidden=5376),
+}
+
+
+def make_proj_inputs(w: ProjWorkload, seed: int = 0) -> dict:
+    """Hidden state, weight slices, gammas and positions of a projection
+    workload.  x: uint16 bf16 bits [L, hidden]; wq, wk, wv: bits [H*D, hidden];
+    gamma_q, gamma_k fp32 [D]; positions int32 [L]; eps and theta."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"x": f32_to_bf16_bits(rng.standard_normal((w.L, w.hidden), dtype=np.float32))}
+    wscale = np.float32(1.0 / math.sqrt(w.hidden))
+    for name in ("wq", "wk", "wv"):
+        out[name] = f32_to_bf16_bits(rng.standard_normal((w.H * w.D, w.hidden), dtype=np.float32) * wscale)
+    out["gamma_q"] = (1.0 + 0.1 * rng.standard_normal(w.D, dtype=np.float32)).astype(np.float32)
+    out["gamma_k"] = (1.0 + 0.1 * rng.standard_normal(w.D, dtype=np.float32)).astype(np.float32)
+    out["positions"] = packed_positions(w.n_video, w.n_audio)
+    out["eps"] = RMS_EPS
+    out["theta"] = ROPE_THETA
+    return out
 
 
 def custom_workload(H: int, L: int, n_audio: int = 0, qk_scale: float = 1.0,
@@ -116,7 +168,7 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     return out
 
 
-def sample_rows(w: Workload, head: int, n: int = 4096, seed: int = 0) -> np.ndarray:
+def sample_rows(w, head: int, n: int = 4096, seed: int = 0) -> np.ndarray:
     """Sorted query rows a sampled check compares for one head.
 
     n distinct rows drawn by Generator(PCG64(seed + 1000 + head)), always

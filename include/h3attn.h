@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   H3_OK = 0,
   H3_ERR_NULL = -1,        /* a required pointer is NULL                          */
-  H3_ERR_SHAPE = -2,       /* H < 1, L < 1, or a size/grid that overflows         */
+  H3_ERR_SHAPE = -2,       /* H < 1, L < 1, a bad hidden size, or an overflow     */
   H3_ERR_UNSUPPORTED = -3, /* D != 128                                            */
   H3_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned             */
   H3_ERR_ALIAS = -5,       /* out overlaps q, k or v; q overlaps k; cos overlaps sin */
@@ -153,6 +153,36 @@ int h3_attention_merge(const float *outs, const float *lses, int P, void *out, f
  */
 int h3_rope_tables(const int *positions, int L, int D, double theta,
                    float *cos, float *sin, void *stream);
+
+/*
+ * The rank's row-sliced qkv projection with QK-RMSNorm + RoPE fused behind
+ * it.  A rank that holds the whole modulated hidden state projects it through
+ * only its own heads' rows of qkv_proj; slicing rows is exact because the
+ * weight's scale is per-tensor ("buqi-minimax-h3-multigpu", How it works: the
+ * all_gather form used at small world sizes; H3's hidden size is 5376).  For
+ * every head h, token t and d < D, with f = h*D + d:
+ *   q~[h][t][d] = sum_c x[t][c] * wq[f][c]    (k~ and v~ likewise)
+ *   q = h3_qknorm_rope's transform of q~ with gamma_q, k likewise with
+ *   gamma_k, v = v~, each rounded once to bf16.
+ * Products are bf16 x bf16 on the matrix cores with fp32 accumulation; the
+ * norm and rotation use the fp32 accumulators directly (no bf16 rounding
+ * before the norm).  No bias.
+ *
+ *   x             bf16 [L][hidden], read only (token-major hidden state).
+ *   wq, wk, wv    bf16 [H*D][hidden] each, read only: the rank's rows of the
+ *                 q, k and v blocks of qkv_proj (nn.Linear layout), e.g.
+ *                 pointer offsets into the full weight.
+ *   gamma_q/_k    fp32 [D];  cos, sin  fp32 [L][D/2] (as for h3_qknorm_rope).
+ *   q, k, v       bf16 [H][L][D], written: the layout h3_attention reads.
+ *                 They must not overlap each other or any input.
+ *   hidden        a positive multiple of 32, at most 2^20.
+ *   eps           > 0 and finite.
+ * All pointers must be 16-byte aligned.
+ */
+int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const void *wv,
+                            const float *gamma_q, const float *gamma_k, const float *cos,
+                            const float *sin, void *q, void *k, void *v, int H, int L,
+                            int hidden, int D, float eps, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *h3_status_string(int status);

@@ -14,4 +14,7 @@ from .h3_oracle import (  # noqa: F401
     attention,
     attention_lse_head,
     merge_partials,
+    qkv_project,
+    split_heads,
+    qkv_proj_qknorm_rope,
 )

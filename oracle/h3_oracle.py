@@ -33,6 +33,15 @@ What it computes (sources are the three pages the build follows):
   and parts combine as out = sum_p exp(lse_p - lse) out_p with
   lse = log sum_p exp(lse_p).
 
+* The row-sliced qkv projection with the prologue behind it.  A rank that
+  receives the whole modulated hidden state projects it through only its own
+  heads' rows of qkv_proj; slicing rows is exact because the weight's scale is
+  per-tensor ("buqi-minimax-h3-multigpu", How it works, the all_gather form
+  used at world_size <= 4; H3 has hidden 5376 and inner 7168 = 56 x 128).
+  Readings: no bias; within each of the q, k and v slices, row h*D + d is
+  head h, dim d; the projection is exact (fp64) and q and k go straight into
+  RMSNorm and RoPE with no rounding in between, then one round to bf16.
+
 Every pin of these functions lives in tests/test_oracle.py.  One part is
 parity unpinned: whether the adjacent-pair RoPE convention and the fp64 tables
 match the real MiniMax-H3 checkpoint (no page states it; the GPU kernel takes
@@ -218,3 +227,41 @@ def merge_partials(outs: np.ndarray, lses: np.ndarray):
     lse = m + np.log(z)
     out = (w[..., None] * outs).sum(axis=0) / z[..., None]
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Row-sliced qkv projection followed by the prologue
+# --------------------------------------------------------------------------
+
+
+def qkv_project(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """y[t, f] = sum_c x[t, c] * w[f, c] in fp64.
+
+    x_bits: bf16 bits [L, C] (tokens x hidden); w_bits: bf16 bits [N, C] (the
+    output features' weight rows, nn.Linear layout).  Returns fp64 [L, N].
+    """
+    return bf16_to_f64(x_bits) @ bf16_to_f64(w_bits).T
+
+
+def split_heads(y: np.ndarray, H: int, D: int = 128) -> np.ndarray:
+    """[L, H*D] -> [H, L, D]: feature h*D + d is head h, dim d."""
+    L = y.shape[0]
+    return np.ascontiguousarray(y.reshape(L, H, D).transpose(1, 0, 2))
+
+
+def qkv_proj_qknorm_rope(x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, cos, sin,
+                         eps: float, H: int, D: int = 128) -> dict:
+    """q, k and v of H heads from the hidden state.
+
+    x_bits [L, C]; wq/wk/wv bits [H*D, C]; gamma fp32 [D]; cos, sin fp32
+    [L, D/2].  q = RoPE(RMSNorm(x Wq^T)), k likewise with gamma_k, v = x Wv^T,
+    each split into heads and rounded once to bf16.  Returns
+    {"q": (fp64 [H, L, D], bits), "k": ..., "v": ...}.
+    """
+    out = {}
+    for name, w, gamma in (("q", wq_bits, gamma_q), ("k", wk_bits, gamma_k), ("v", wv_bits, None)):
+        y = split_heads(qkv_project(x_bits, w), H, D)
+        if gamma is not None:
+            y = rope_rotate(rms_norm(y, gamma, eps), cos[None], sin[None])
+        out[name] = (y, f64_to_bf16_bits(y))
+    return out

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
-              "h3_status_string", "h3_abi_version"):
+              "h3_qkv_proj_qknorm_rope", "h3_status_string", "h3_abi_version"):
         assert n in names
 
 
@@ -131,3 +131,22 @@ def test_attention_merge_argument_errors(B):
     assert _merge(B, outs=A + 4) == -4 and _merge(B, lse_out=A + 192 * MB + 1) == -4
     assert _merge(B, out=A + 16) == -5                     # out inside outs
     assert _merge(B, lse_out=A + 128 * MB) == -5           # lse_out over out
+
+
+def _qkv(B, x=A, wq=A + 1 * MB, wk=A + 2 * MB, wv=A + 3 * MB, gq=A + 4 * MB, gk=A + 5 * MB, c=A + 6 * MB,
+         s=A + 7 * MB, q=A + 8 * MB, k=A + 9 * MB, v=A + 10 * MB, H=2, L=512, C=256, D=128, eps=1e-6):
+    return B.lib.h3_qkv_proj_qknorm_rope(x, wq, wk, wv, gq, gk, c, s, q, k, v, H, L, C, D, eps, None)
+
+
+def test_qkv_proj_argument_errors(B):
+    assert _qkv(B, x=None) == -1 and _qkv(B, wv=None) == -1 and _qkv(B, v=None) == -1 and _qkv(B, s=None) == -1
+    assert _qkv(B, H=0) == -2 and _qkv(B, L=0) == -2
+    assert _qkv(B, C=0) == -2 and _qkv(B, C=48) == -2 and _qkv(B, C=(1 << 20) + 32) == -2
+    assert _qkv(B, H=1 << 16, L=1 << 16) == -2
+    assert _qkv(B, D=64) == -3
+    assert _qkv(B, x=A + 8) == -4 and _qkv(B, gk=A + 5 * MB + 4) == -4 and _qkv(B, k=A + 9 * MB + 2) == -4
+    assert _qkv(B, q=A + 16) == -5                         # q over x
+    assert _qkv(B, v=A + 3 * MB) == -5                     # v over wv
+    assert _qkv(B, k=A + 8 * MB + 64) == -5                # k inside q
+    assert _qkv(B, q=A + 6 * MB) == -5                     # q over cos
+    assert _qkv(B, eps=0.0) == -6 and _qkv(B, eps=float("inf")) == -6

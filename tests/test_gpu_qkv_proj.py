@@ -1,0 +1,140 @@
+"""GPU parity of h3_qkv_proj_qknorm_rope (row-sliced qkv projection with
+QK-RMSNorm + RoPE fused behind it) against the oracle, through the C ABI.
+
+Bar, per element z of q, k and v against the exact fp64 value:
+    |gpu - z| <= spacing_bf16(z) + 2^-16 * max_row |z|
+The spacing term is the final round to bf16 of a slightly different fp32
+value.  The second term covers the fp32 work before it: the accumulation of
+hidden/16 matrix-core block sums (a random walk of ~2^-24-relative roundings,
+~1e-6 of |z| at hidden = 5376), and for q and k the norm and rotation, whose
+fp32 roundings scale with the row's largest term (as for h3_qknorm_rope).
+2^-16 leaves 10x room over those and stays 500x under one bf16 spacing at the
+row's largest element, so a wrong weight row, token, head or pairing fails.
+Elements that differ from RNE(z) at all must be rarer than 1e-3 (near-ties).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_head_attention_amd import inputs as I
+from tests.gpu_helpers import ATTN_TOL, bits, row_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload(x):
+    import torch
+    d = {n: to_dev(x[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv")}
+    d.update(gamma_q=to_dev(x["gamma_q"], torch.float32), gamma_k=to_dev(x["gamma_k"], torch.float32),
+             positions=to_dev(x["positions"], torch.int32))
+    return d
+
+
+def _check(label, got_bits, ref, ref_bits):
+    mag = np.abs(ref)
+    spacing = np.exp2(np.maximum(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7, -133))
+    slack = spacing + 2.0 ** -16 * mag.max(axis=-1, keepdims=True)
+    err = np.abs(oracle.bf16_to_f64(got_bits) - ref)
+    ratio = float((err / slack).max())
+    mism = float(np.mean(got_bits != ref_bits))
+    rel = float(row_rel_err(got_bits.reshape(-1, 128), ref.reshape(-1, 128)).max())
+    print(f"{label}: max err/bound {ratio:.3f}, mismatch vs RNE(exact) {mism:.2e}, max row rel {rel:.2e}")
+    assert ratio <= 1.0
+    assert mism < 1e-3
+    assert rel <= ATTN_TOL
+
+
+def _run(gpu_lib, x, H, rows=None, label=""):
+    """Project on the GPU; compare all heads of q, k, v on the given tokens
+    (all tokens if rows is None) with the oracle."""
+    import torch
+    d = _upload(x)
+    cos, sin = gpu_lib.rope_tables(d["positions"], 128, x["theta"])
+    q, k, v = gpu_lib.qkv_proj_qknorm_rope(d["x"], d["wq"], d["wk"], d["wv"], d["gamma_q"], d["gamma_k"],
+                                           cos, sin, x["eps"])
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.rope_tables(x["positions"], 128, x["theta"])
+    xs = x["x"] if rows is None else x["x"][rows]
+    cr, sr = (c_ref, s_ref) if rows is None else (c_ref[rows], s_ref[rows])
+    ref = oracle.qkv_proj_qknorm_rope(xs, x["wq"], x["wk"], x["wv"], x["gamma_q"], x["gamma_k"], cr, sr,
+                                      x["eps"], H)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        got = bits(t)
+        if rows is not None:
+            got = got[:, rows]
+        _check(f"{label} {name}", got, *ref[name])
+    return q, k, v
+
+
+def _custom(H, L, hidden, n_audio, seed):
+    w = I.ProjWorkload(f"H{H}_L{L}_C{hidden}", H=H, L=L, n_video=L - n_audio, n_audio=n_audio, hidden=hidden)
+    return w, I.make_proj_inputs(w, seed)
+
+
+def test_qkv_proj_tiny_all_elements(gpu_lib):
+    w = I.PROJ_WORKLOADS["proj_tiny"]
+    _run(gpu_lib, I.make_proj_inputs(w, 0), w.H, label="proj_tiny")
+
+
+@pytest.mark.parametrize("H,L,hidden", [(1, 1, 32), (1, 7, 64), (3, 257, 96), (2, 513, 160)])
+def test_qkv_proj_ragged_shapes_all_elements(gpu_lib, H, L, hidden):
+    """One token, a single hidden step, token counts one past a tile, hidden
+    sizes that are odd multiples of the 32-element step."""
+    w, x = _custom(H, L, hidden, n_audio=L // 3, seed=100 + L)
+    _run(gpu_lib, x, H, label=f"H={H} L={L} hidden={hidden}")
+
+
+def test_qkv_proj_ws8_sampled(gpu_lib):
+    """H = 7, L = 32768, hidden 5376: 1024 sampled tokens (segment boundaries
+    included), every head and feature of q, k and v."""
+    w = I.PROJ_WORKLOADS["proj_ws8"]
+    x = I.make_proj_inputs(w, 0)
+    _run(gpu_lib, x, w.H, rows=I.sample_rows(w, 0, 1024), label="proj_ws8")
+
+
+@pytest.mark.timeout(600)
+def test_qkv_proj_ws2_sampled(gpu_lib):
+    """H = 28 (the all_gather form at world_size 2), 512 sampled tokens."""
+    w = I.PROJ_WORKLOADS["proj_ws2"]
+    x = I.make_proj_inputs(w, 0)
+    _run(gpu_lib, x, w.H, rows=I.sample_rows(w, 0, 512), label="proj_ws2")
+
+
+def test_qkv_proj_head_slices_bit_identical(gpu_lib):
+    """Four heads in one launch against two launches of two heads each, fed
+    row slices of the same weights (pointer offsets): every head of q, k and
+    v bit-identical."""
+    import torch
+    w, x = _custom(4, 1000, 512, n_audio=100, seed=7)
+    d = _upload(x)
+    cos, sin = gpu_lib.rope_tables(d["positions"], 128, x["theta"])
+    args = (d["gamma_q"], d["gamma_k"], cos, sin, x["eps"])
+    full = gpu_lib.qkv_proj_qknorm_rope(d["x"], d["wq"], d["wk"], d["wv"], *args)
+    parts = [gpu_lib.qkv_proj_qknorm_rope(d["x"], d["wq"][r:r + 256], d["wk"][r:r + 256], d["wv"][r:r + 256],
+                                          *args) for r in (0, 256)]
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(full[i][:2], parts[0][i]) and torch.equal(full[i][2:], parts[1][i])
+
+
+def test_qkv_proj_then_attention_chain(gpu_lib):
+    """Projection (with the fused prologue) then attention on the GPU, against
+    the all-oracle chain: per-row relative error within the attention bar."""
+    import torch
+    w = I.PROJ_WORKLOADS["proj_tiny"]
+    x = I.make_proj_inputs(w, 1)
+    d = _upload(x)
+    cos, sin = gpu_lib.rope_tables(d["positions"], 128, x["theta"])
+    q, k, v = gpu_lib.qkv_proj_qknorm_rope(d["x"], d["wq"], d["wk"], d["wv"], d["gamma_q"], d["gamma_k"],
+                                           cos, sin, x["eps"])
+    out = gpu_lib.attention(q, k, v, scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.rope_tables(x["positions"], 128, x["theta"])
+    ref = oracle.qkv_proj_qknorm_rope(x["x"], x["wq"], x["wk"], x["wv"], x["gamma_q"], x["gamma_k"], c_ref,
+                                      s_ref, x["eps"], w.H)
+    o_ref = oracle.attention(ref["q"][1], ref["k"][1], ref["v"][1], 1 / math.sqrt(128))
+    err = row_rel_err(bits(out).reshape(-1, 128), o_ref.reshape(-1, 128))
+    print(f"projection -> attention chain: max row rel err {err.max():.3e}")
+    assert err.max() <= ATTN_TOL

@@ -49,3 +49,16 @@ def test_sample_rows_contains_boundaries():
     assert np.array_equal(r, I.sample_rows(w, head=3, n=4096))
     assert not np.array_equal(r, I.sample_rows(w, head=4, n=4096))
     assert np.array_equal(I.sample_rows(I.WORKLOADS["tiny"], 0, 4096), np.arange(512))
+
+
+def test_projection_inputs():
+    w = I.PROJ_WORKLOADS["proj_tiny"]
+    a, b = I.make_proj_inputs(w, seed=0), I.make_proj_inputs(w, seed=0)
+    for key in ("x", "wq", "wk", "wv", "gamma_q", "gamma_k", "positions"):
+        assert np.array_equal(a[key], b[key])
+    assert a["x"].shape == (300, 512) and a["wq"].shape == (256, 512) and a["x"].dtype == np.uint16
+    wf = (a["wv"].astype(np.uint32) << 16).view(np.float32)
+    assert abs(float(wf.std()) * np.sqrt(512) - 1.0) < 0.05
+    assert not np.array_equal(a["wq"], a["wk"])
+    assert I.PROJ_WORKLOADS["proj_ws2"].hidden == 5376 and I.PROJ_WORKLOADS["proj_ws2"].H == 28
+    assert I.PROJ_WORKLOADS["proj_ws2"].flops == 2.0 * 32768 * 3 * 28 * 128 * 5376

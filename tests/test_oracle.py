@@ -435,3 +435,103 @@ def test_merge_single_part_and_empty_part():
                                   np.stack([l1, np.full((2, 5), -np.inf)]))
     np.testing.assert_allclose(out2, o1, rtol=1e-15)
     np.testing.assert_allclose(lse2, l1, rtol=1e-15)
+
+
+# ------------------------------------------- qkv projection + fused prologue
+
+
+def _rand_bits(rng, shape, std=1.0):
+    return _bits_of(std * rng.standard_normal(shape))
+
+
+def test_qkv_project_brute_force():
+    """Brute force with pure-Python loops: y[t, f] = sum_c x[t, c] w[f, c]."""
+    rng = np.random.default_rng(11)
+    x, w = _rand_bits(rng, (3, 7)), _rand_bits(rng, (5, 7))
+    xf, wf = O.bf16_to_f64(x), O.bf16_to_f64(w)
+    y = O.qkv_project(x, w)
+    assert y.shape == (3, 5)
+    for t in range(3):
+        for f in range(5):
+            ref = 0.0
+            for c in range(7):
+                ref += float(xf[t, c]) * float(wf[f, c])
+            assert abs(y[t, f] - ref) <= 1e-14 * (1 + abs(ref))
+
+
+def test_qkv_split_heads_element_definition():
+    """Brute force on a few elements: head h, dim d of v is feature h*D + d of
+    the projection, for token t (the head split's reading)."""
+    rng = np.random.default_rng(12)
+    H, D, L, C = 2, 128, 5, 40
+    x, wv = _rand_bits(rng, (L, C)), _rand_bits(rng, (H * D, C), 0.2)
+    wq = wk = _rand_bits(rng, (H * D, C), 0.2)
+    cos, sin = O.rope_tables(np.arange(L), D)
+    v = O.qkv_proj_qknorm_rope(x, wq, wk, wv, np.ones(D, np.float32), np.ones(D, np.float32),
+                               cos, sin, 1e-6, H)["v"][0]
+    xf, wf = O.bf16_to_f64(x), O.bf16_to_f64(wv)
+    for h, t, d in ((0, 0, 0), (1, 4, 127), (1, 2, 5), (0, 3, 64)):
+        ref = sum(float(xf[t, c]) * float(wf[h * D + d, c]) for c in range(C))
+        assert abs(v[h, t, d] - ref) <= 1e-14 * (1 + abs(ref))
+
+
+def test_qkv_one_hot_weights_reduce_to_the_prologue():
+    """Special case: one-hot weight rows select hidden columns exactly, so the
+    fused chain must equal the (separately pinned) prologue applied to those
+    columns, bit for bit, and v must be the selected columns themselves."""
+    rng = np.random.default_rng(13)
+    H, D, L, C = 2, 128, 37, 3 * 2 * 128 + 20
+    x = _rand_bits(rng, (L, C))
+    perm = rng.permutation(C)
+    sel = {n: perm[i * H * D:(i + 1) * H * D] for i, n in enumerate("qkv")}
+    one = O.f64_to_bf16_bits(np.array([1.0]))[0]
+
+    def onehot(cols):
+        w = np.zeros((len(cols), C), np.uint16)
+        w[np.arange(len(cols)), cols] = one
+        return w
+
+    gq = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    gk = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    cos, sin = O.rope_tables(np.arange(L), D)
+    res = O.qkv_proj_qknorm_rope(x, onehot(sel["q"]), onehot(sel["k"]), onehot(sel["v"]), gq, gk,
+                                 cos, sin, 1e-6, H)
+    for n, g in (("q", gq), ("k", gk)):
+        cols = x[:, sel[n]].reshape(L, H, D).transpose(1, 0, 2)
+        y_ref, b_ref = O.qknorm_rope(cols, g, cos, sin, 1e-6)
+        assert np.array_equal(res[n][1], b_ref)
+        np.testing.assert_allclose(res[n][0], y_ref, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(res["v"][1], x[:, sel["v"]].reshape(L, H, D).transpose(1, 0, 2))
+
+
+def test_qkv_norm_removes_weight_scale_but_v_keeps_it():
+    """Invariant: RMSNorm(2y) = RMSNorm(y) up to eps, so doubling the weights
+    (exact in bf16) leaves q and k unchanged and doubles v exactly."""
+    rng = np.random.default_rng(14)
+    H, D, L, C = 1, 128, 9, 64
+    x = _rand_bits(rng, (L, C))
+    w = {n: _rand_bits(rng, (H * D, C), 0.3) for n in "qkv"}
+    w2 = {n: O.f64_to_bf16_bits(2 * O.bf16_to_f64(b)) for n, b in w.items()}
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    cos, sin = O.rope_tables(np.arange(L), D)
+    a = O.qkv_proj_qknorm_rope(x, w["q"], w["k"], w["v"], g, g, cos, sin, 1e-12, H)
+    b = O.qkv_proj_qknorm_rope(x, w2["q"], w2["k"], w2["v"], g, g, cos, sin, 1e-12, H)
+    for n in "qk":
+        np.testing.assert_allclose(b[n][0], a[n][0], rtol=1e-9, atol=1e-12)
+    assert np.array_equal(b["v"][0], 2 * a["v"][0])
+
+
+def test_qkv_head_permutation_equivariance():
+    """Invariant: swapping the two heads' weight row blocks swaps the output
+    heads (norm and rotation act per head with shared gamma and tables)."""
+    rng = np.random.default_rng(15)
+    H, D, L, C = 2, 128, 6, 48
+    x = _rand_bits(rng, (L, C))
+    w = {n: _rand_bits(rng, (H * D, C), 0.3) for n in "qkv"}
+    sw = {n: np.concatenate([b[D:], b[:D]]) for n, b in w.items()}
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    cos, sin = O.rope_tables(np.arange(L) * 7, D)
+    a = O.qkv_proj_qknorm_rope(x, w["q"], w["k"], w["v"], g, g, cos, sin, 1e-6, H)
+    b = O.qkv_proj_qknorm_rope(x, sw["q"], sw["k"], sw["v"], g, g, cos, sin, 1e-6, H)
+    for n in "qkv":
+        assert np.array_equal(b[n][1], a[n][1][::-1])

@@ -102,6 +102,27 @@ def _lse_missing_log(q, k, v, scale, block=256):
     return out, s.max(axis=1) + np.exp(lse - s.max(axis=1))
 
 
+def _split_heads_dim_major(y, H, D=128):
+    L = y.shape[0]
+    return np.ascontiguousarray(y.reshape(L, D, H).transpose(2, 0, 1))
+
+
+def _project_no_transpose_rows(x_bits, w_bits):
+    # uses the weight's columns in reverse order (a transposed/reversed operand)
+    return H.bf16_to_f64(x_bits) @ H.bf16_to_f64(w_bits)[:, ::-1].T
+
+
+def _qkv_norms_v_too(x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, cos, sin, eps, Hh, D=128):
+    out = H.__dict__["_orig_qkv"](x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, cos, sin, eps, Hh, D)
+    y = H.rope_rotate(H.rms_norm(out["v"][0], gamma_k, eps), cos[None], sin[None])
+    out["v"] = (y, H.f64_to_bf16_bits(y))
+    return out
+
+
+def _qkv_swapped_gammas(x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, cos, sin, eps, Hh, D=128):
+    return H.__dict__["_orig_qkv"](x_bits, wq_bits, wk_bits, wv_bits, gamma_k, gamma_q, cos, sin, eps, Hh, D)
+
+
 PIN_TESTS = [getattr(T, n) for n in dir(T) if n.startswith("test_")]
 
 MUTANTS = {
@@ -120,6 +141,10 @@ MUTANTS = {
     "attn_softmax_wrong_axis": ("attention_head", _attn_softmax_over_queries),
     "merge_linear_weights": ("merge_partials", _merge_linear_weights),
     "lse_missing_log": ("attention_lse_head", _lse_missing_log),
+    "split_heads_dim_major": ("split_heads", _split_heads_dim_major),
+    "project_reversed_operand": ("qkv_project", _project_no_transpose_rows),
+    "qkv_norms_v": ("qkv_proj_qknorm_rope", _qkv_norms_v_too),
+    "qkv_swapped_gammas": ("qkv_proj_qknorm_rope", _qkv_swapped_gammas),
 }
 
 
@@ -128,6 +153,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     fn_name, mutant = MUTANTS[name]
     monkeypatch.setitem(H.__dict__, "_orig_attention_head", H.attention_head)
     monkeypatch.setitem(H.__dict__, "_orig_attention_lse_head", H.attention_lse_head)
+    monkeypatch.setitem(H.__dict__, "_orig_qkv", H.qkv_proj_qknorm_rope)
     monkeypatch.setattr(H, fn_name, mutant)
     monkeypatch.setattr(oracle, fn_name, mutant)
     failed = []
