@@ -17,4 +17,6 @@ from .h3_oracle import (  # noqa: F401
     qkv_project,
     split_heads,
     qkv_proj_qknorm_rope,
+    e4m3_to_f64,
+    qkv_proj_fp8_qknorm_rope,
 )

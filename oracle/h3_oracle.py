@@ -41,6 +41,12 @@ What it computes (sources are the three pages the build follows):
   Readings: no bias; within each of the q, k and v slices, row h*D + d is
   head h, dim d; the projection is exact (fp64) and q and k go straight into
   RMSNorm and RoPE with no rounding in between, then one round to bf16.
+  The fp8 form (the checkpoint the page recommends stores fp8 weights with
+  one scale per tensor): hidden state and weight rows are OCP e4m3 codes
+  with one fp32 scale each, and the projection is
+  x_scale * w_scale * sum_c x8[t, c] * w8[f, c], exact in fp64.  Reading:
+  both operands are fp8 (the pages' transformer GEMMs run in fp8) and the
+  scales multiply the exact dot product before the norm.
 
 Every pin of these functions lives in tests/test_oracle.py.  One part is
 parity unpinned: whether the adjacent-pair RoPE convention and the fp64 tables
@@ -261,6 +267,41 @@ def qkv_proj_qknorm_rope(x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, co
     out = {}
     for name, w, gamma in (("q", wq_bits, gamma_q), ("k", wk_bits, gamma_k), ("v", wv_bits, None)):
         y = split_heads(qkv_project(x_bits, w), H, D)
+        if gamma is not None:
+            y = rope_rotate(rms_norm(y, gamma, eps), cos[None], sin[None])
+        out[name] = (y, f64_to_bf16_bits(y))
+    return out
+
+
+# --------------------------------------------------------------------------
+# fp8 (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+# infinities; exponent and mantissa all ones is NaN)
+# --------------------------------------------------------------------------
+
+
+def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode e4m3 codes exactly: normal (1 + m/8) 2^(e-7) for e >= 1,
+    subnormal (m/8) 2^-6 for e = 0, NaN for the two all-ones codes."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & ((b & 7) == 7), np.nan, out)
+
+
+def qkv_proj_fp8_qknorm_rope(x8, x_scale, wq8, wk8, wv8, w_scale, gamma_q, gamma_k, cos, sin,
+                             eps: float, H: int, D: int = 128) -> dict:
+    """The fp8 form of qkv_proj_qknorm_rope: x8 e4m3 codes [L, C] with scale
+    x_scale, weight rows e4m3 [H*D, C] with the per-tensor scale w_scale;
+    y = x_scale * w_scale * (x8 w8^T) exactly, then the same head split,
+    RMSNorm + RoPE for q and k, and one round to bf16."""
+    xf = e4m3_to_f64(x8)
+    out = {}
+    for name, w, gamma in (("q", wq8, gamma_q), ("k", wk8, gamma_k), ("v", wv8, None)):
+        y = float(x_scale) * float(w_scale) * (xf @ e4m3_to_f64(w).T)
+        y = split_heads(y, H, D)
         if gamma is not None:
             y = rope_rotate(rms_norm(y, gamma, eps), cos[None], sin[None])
         out[name] = (y, f64_to_bf16_bits(y))

@@ -535,3 +535,55 @@ def test_qkv_head_permutation_equivariance():
     b = O.qkv_proj_qknorm_rope(x, sw["q"], sw["k"], sw["v"], g, g, cos, sin, 1e-6, H)
     for n in "qkv":
         assert np.array_equal(b[n][1], a[n][1][::-1])
+
+
+# ---------------------------------------------------------------- fp8 e4m3
+
+
+def test_e4m3_known_codes():
+    """Closed form: the OCP e4m3 encoding's landmark codes."""
+    vals = O.e4m3_to_f64(np.array([0x00, 0x80, 0x38, 0xB8, 0x7E, 0x08, 0x07, 0x01, 0x40, 0x3C], np.uint8))
+    assert vals[0] == 0.0 and vals[1] == 0.0 and math.copysign(1, vals[1]) == -1
+    assert vals[2] == 1.0 and vals[3] == -1.0
+    assert vals[4] == 448.0                        # largest finite
+    assert vals[5] == 2.0 ** -6                    # smallest normal
+    assert vals[6] == 7 / 8 * 2.0 ** -6 and vals[7] == 2.0 ** -9   # subnormals
+    assert vals[8] == 2.0 and vals[9] == 1.5
+    assert np.isnan(O.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_e4m3_matches_torch_exhaustive():
+    """Library routine, all 256 codes: torch's float8_e4m3fn decoding."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp8_projection_brute_force_and_scales():
+    """Brute force with loops on a tiny case: v = x_scale * w_scale *
+    sum_c x[t, c] w[f, c]; q and k equal the bf16 form's prologue applied to
+    the same (exactly representable) projection."""
+    rng = np.random.default_rng(21)
+    H, D, L, C = 1, 128, 3, 8
+    x8 = rng.integers(0, 256, (L, C), dtype=np.uint8)
+    x8[(x8 & 0x7F) == 0x7F] = 0x38                 # no NaN codes
+    w8 = {n: rng.integers(0, 256, (H * D, C), dtype=np.uint8) for n in "qkv"}
+    for n in w8:
+        w8[n][(w8[n] & 0x7F) == 0x7F] = 0x30
+    sx, sw = 0.375, 1.0 / 64
+    g = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    cos, sin = O.rope_tables(np.arange(L), D)
+    res = O.qkv_proj_fp8_qknorm_rope(x8, sx, w8["q"], w8["k"], w8["v"], sw, g, g, cos, sin, 1e-6, H)
+    xf, wf = O.e4m3_to_f64(x8), O.e4m3_to_f64(w8["v"])
+    for t in range(L):
+        for f in (0, 5, 127):
+            ref = 0.0
+            for c in range(C):
+                ref += float(xf[t, c]) * float(wf[f, c])
+            assert abs(res["v"][0][0, t, f] - sx * sw * ref) <= 1e-12 * (1 + abs(sx * sw * ref))
+    yq = sx * sw * (xf @ O.e4m3_to_f64(w8["q"]).T)
+    ref_q = O.rope_rotate(O.rms_norm(yq.reshape(L, H, D).transpose(1, 0, 2), g, 1e-6), cos[None], sin[None])
+    np.testing.assert_allclose(res["q"][0], ref_q, rtol=1e-12, atol=1e-12)

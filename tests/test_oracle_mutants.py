@@ -123,6 +123,17 @@ def _qkv_swapped_gammas(x_bits, wq_bits, wk_bits, wv_bits, gamma_q, gamma_k, cos
     return H.__dict__["_orig_qkv"](x_bits, wq_bits, wk_bits, wv_bits, gamma_k, gamma_q, cos, sin, eps, Hh, D)
 
 
+def _e4m3_bias8(bits):
+    return H.__dict__["_orig_e4m3"](bits) / 2.0
+
+
+def _fp8_scale_dropped_for_qk(x8, x_scale, wq8, wk8, wv8, w_scale, gamma_q, gamma_k, cos, sin, eps, Hh, D=128):
+    out = H.__dict__["_orig_qkv8"](x8, 1.0, wq8, wk8, wv8, 1.0, gamma_q, gamma_k, cos, sin, eps, Hh, D)
+    ref = H.__dict__["_orig_qkv8"](x8, x_scale, wq8, wk8, wv8, w_scale, gamma_q, gamma_k, cos, sin, eps, Hh, D)
+    out["v"] = ref["v"]
+    return out
+
+
 PIN_TESTS = [getattr(T, n) for n in dir(T) if n.startswith("test_")]
 
 MUTANTS = {
@@ -145,6 +156,8 @@ MUTANTS = {
     "project_reversed_operand": ("qkv_project", _project_no_transpose_rows),
     "qkv_norms_v": ("qkv_proj_qknorm_rope", _qkv_norms_v_too),
     "qkv_swapped_gammas": ("qkv_proj_qknorm_rope", _qkv_swapped_gammas),
+    "e4m3_bias8": ("e4m3_to_f64", _e4m3_bias8),
+    "fp8_scale_dropped_for_qk": ("qkv_proj_fp8_qknorm_rope", _fp8_scale_dropped_for_qk),
 }
 
 
@@ -154,6 +167,8 @@ def test_pins_catch_mutant(name, monkeypatch):
     monkeypatch.setitem(H.__dict__, "_orig_attention_head", H.attention_head)
     monkeypatch.setitem(H.__dict__, "_orig_attention_lse_head", H.attention_lse_head)
     monkeypatch.setitem(H.__dict__, "_orig_qkv", H.qkv_proj_qknorm_rope)
+    monkeypatch.setitem(H.__dict__, "_orig_e4m3", H.e4m3_to_f64)
+    monkeypatch.setitem(H.__dict__, "_orig_qkv8", H.qkv_proj_fp8_qknorm_rope)
     monkeypatch.setattr(H, fn_name, mutant)
     monkeypatch.setattr(oracle, fn_name, mutant)
     failed = []
