@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E peak
 CALIB_COPY_BYTES = 512 << 20        # plain device copy whose counters calibrate FETCH/WRITE_SIZE
 ATTN_SOURCE = os.path.join(ROOT, "exact_head_attention_amd", "csrc", "attn_fwd.hip")
@@ -178,14 +179,22 @@ def bench_projection(args):
             a = a.view(np.int16)
         return torch.from_numpy(a).view(dt).to(dev)
 
-    xs, wq, wk, wv = (up(x[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv"))
     gq, gk = up(x["gamma_q"], torch.float32), up(x["gamma_k"], torch.float32)
     cos, sin = B.rope_tables(up(x["positions"], torch.int32), w.D, x["theta"])
     outs = tuple(torch.empty((w.H, w.L, w.D), dtype=torch.bfloat16, device=dev) for _ in range(3))
     stream = torch.cuda.current_stream()
+    if w.fp8:
+        xs, wq, wk, wv = (up(x[n], torch.uint8).view(torch.float8_e4m3fn) for n in ("x", "wq", "wk", "wv"))
+        sx = up(np.array([x["x_scale"]], np.float32), torch.float32)
+        sw = up(np.array([x["w_scale"]], np.float32), torch.float32)
 
-    def call():
-        B.qkv_proj_qknorm_rope(xs, wq, wk, wv, gq, gk, cos, sin, x["eps"], out=outs)
+        def call():
+            B.qkv_proj_fp8_qknorm_rope(xs, sx, wq, wk, wv, sw, gq, gk, cos, sin, x["eps"], out=outs)
+    else:
+        xs, wq, wk, wv = (up(x[n], torch.bfloat16) for n in ("x", "wq", "wk", "wv"))
+
+        def call():
+            B.qkv_proj_qknorm_rope(xs, wq, wk, wv, gq, gk, cos, sin, x["eps"], out=outs)
 
     for _ in range(args.warmup):
         call()
@@ -201,18 +210,21 @@ def bench_projection(args):
     tflops = w.flops / (ms / 1e3) / 1e12
     # HBM bytes the call must move: x and the weight slices read once, q, k, v
     # written once, tables and gammas read once.
-    bytes_alg = 2 * w.L * w.hidden + 3 * 2 * w.H * w.D * w.hidden + 3 * 2 * w.H * w.L * w.D + 2 * 4 * w.L * 64
+    eb = 1 if w.fp8 else 2
+    bytes_alg = eb * w.L * w.hidden + 3 * eb * w.H * w.D * w.hidden + 3 * 2 * w.H * w.L * w.D + 2 * 4 * w.L * 64
+    peak = FP8_MFMA_PEAK_TFLOPS if w.fp8 else BF16_MFMA_PEAK_TFLOPS
     rec = {
-        "metric": "qkv projection TFLOPS (2*L*3*H*D*hidden per call, QK-norm + RoPE fused) and % bf16 MFMA peak",
+        "metric": "qkv projection TFLOPS (2*L*3*H*D*hidden per call, QK-norm + RoPE fused) and % MFMA peak",
         "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded N(0,1) hidden state, N(0,1/hidden) weights)",
+        "dtype": "fp8 e4m3 (fp32 accumulation)" if w.fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) hidden state, N(0,1/hidden) weights)",
         "config": {"workload": f"{w.name}: row-sliced qkv_proj of H={w.H} heads over L={w.L} tokens, "
                                f"hidden={w.hidden}, D={w.D}", "H": w.H, "L": w.L, "hidden": w.hidden,
                    "seed": args.seed},
-        "roofline": {"kernel": "qkv_proj_kernel", "bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+        "roofline": {"kernel": f"qkv_proj_kernel<{'true' if w.fp8 else 'false'}>", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
                      "avg_launch_ms": round(ms, 4), "min_launch_ms": round(min(ms_all), 4),
                      "flops_per_launch": w.flops, "algorithmic_bytes": bytes_alg},
     }

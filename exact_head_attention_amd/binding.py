@@ -34,6 +34,8 @@ lib.h3_attention_merge.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp]
 lib.h3_attention_merge.restype = _i
 lib.h3_qkv_proj_qknorm_rope.argtypes = [_vp] * 11 + [_i, _i, _i, _i, _f, _vp]
 lib.h3_qkv_proj_qknorm_rope.restype = _i
+lib.h3_qkv_proj_fp8_qknorm_rope.argtypes = [_vp] * 13 + [_i, _i, _i, _i, _f, _vp]
+lib.h3_qkv_proj_fp8_qknorm_rope.restype = _i
 lib.h3_status_string.argtypes = [_i]
 lib.h3_status_string.restype = ctypes.c_char_p
 lib.h3_abi_version.argtypes = []
@@ -41,7 +43,7 @@ lib.h3_abi_version.restype = _i
 
 HEAD_DIM = 128
 EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
-            "h3_qkv_proj_qknorm_rope", "h3_status_string", "h3_abi_version")
+            "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope", "h3_status_string", "h3_abi_version")
 
 
 class H3Error(RuntimeError):
@@ -202,6 +204,41 @@ def qkv_proj_qknorm_rope(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, eps: float =
     _check("h3_qkv_proj_qknorm_rope", lib.h3_qkv_proj_qknorm_rope(
         _dev(x, torch.bfloat16, "x"), _dev(wq, torch.bfloat16, "wq"), _dev(wk, torch.bfloat16, "wk"),
         _dev(wv, torch.bfloat16, "wv"), _dev(gamma_q, torch.float32, "gamma_q"),
+        _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
+        _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
+        _dev(out[2], torch.bfloat16, "v"), H, L, C, HEAD_DIM, float(eps), _stream()))
+    return out
+
+
+def qkv_proj_fp8_qknorm_rope(x, x_scale, wq, wk, wv, w_scale, gamma_q, gamma_k, cos, sin, eps: float = 1e-6,
+                             out=None):
+    """The fp8 form: x float8_e4m3fn [L, hidden] with x_scale (fp32 tensor of
+    one element), wq/wk/wv float8_e4m3fn [H*128, hidden] with the weight's
+    per-tensor w_scale.  Returns (q, k, v), bf16 [H, L, 128] each."""
+    import torch
+    f8 = torch.float8_e4m3fn
+    if x.dim() != 2:
+        raise ValueError(f"x must be [L, hidden], got {tuple(x.shape)}")
+    L, C = x.shape
+    if wq.dim() != 2 or wq.shape[1] != C or wq.shape[0] % HEAD_DIM:
+        raise ValueError(f"wq must be [H*{HEAD_DIM}, {C}], got {tuple(wq.shape)}")
+    if tuple(wk.shape) != tuple(wq.shape) or tuple(wv.shape) != tuple(wq.shape):
+        raise ValueError("wq, wk and wv must have the same shape")
+    if x_scale.numel() != 1 or w_scale.numel() != 1:
+        raise ValueError("x_scale and w_scale must hold one element each")
+    H = wq.shape[0] // HEAD_DIM
+    if tuple(cos.shape) != (L, HEAD_DIM // 2) or tuple(sin.shape) != (L, HEAD_DIM // 2):
+        raise ValueError(f"cos/sin must be [{L}, {HEAD_DIM // 2}]")
+    if gamma_q.numel() != HEAD_DIM or gamma_k.numel() != HEAD_DIM:
+        raise ValueError(f"gamma_q/gamma_k must have {HEAD_DIM} elements")
+    if out is None:
+        out = tuple(torch.empty((H, L, HEAD_DIM), dtype=torch.bfloat16, device=x.device) for _ in range(3))
+    for t, n in zip(out, "qkv"):
+        if tuple(t.shape) != (H, L, HEAD_DIM):
+            raise ValueError(f"out {n} must be [{H}, {L}, {HEAD_DIM}]")
+    _check("h3_qkv_proj_fp8_qknorm_rope", lib.h3_qkv_proj_fp8_qknorm_rope(
+        _dev(x, f8, "x"), _dev(x_scale, torch.float32, "x_scale"), _dev(wq, f8, "wq"), _dev(wk, f8, "wk"),
+        _dev(wv, f8, "wv"), _dev(w_scale, torch.float32, "w_scale"), _dev(gamma_q, torch.float32, "gamma_q"),
         _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
         _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
         _dev(out[2], torch.bfloat16, "v"), H, L, C, HEAD_DIM, float(eps), _stream()))

@@ -38,7 +38,7 @@ const char *h3_status_string(int status) {
   switch (status) {
     case H3_OK: return "ok";
     case H3_ERR_NULL: return "a required pointer is NULL";
-    case H3_ERR_SHAPE: return "a size is out of range (H, L >= 1, H*L < 2^31, hidden a multiple of 32)";
+    case H3_ERR_SHAPE: return "a size is out of range (H, L >= 1, H*L < 2^31, hidden a multiple of the step)";
     case H3_ERR_UNSUPPORTED: return "only head_dim D == 128 is supported";
     case H3_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case H3_ERR_ALIAS: return "output and input buffers overlap";
@@ -155,37 +155,69 @@ int h3_rope_tables(const int *positions, int L, int D, double theta,
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 
-int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const void *wv,
-                            const float *gamma_q, const float *gamma_k, const float *cos,
-                            const float *sin, void *q, void *k, void *v, int H, int L,
-                            int hidden, int D, float eps, void *stream) {
+// Shared checks of the two projection entry points (elem = bytes per hidden
+// element; scales = the fp8 form's two device scalars, else null).
+static int check_qkv_proj(const void *x, const void *wq, const void *wk, const void *wv, const float *x_scale,
+                          const float *w_scale, bool fp8, const float *gamma_q, const float *gamma_k,
+                          const float *cos, const float *sin, void *q, void *k, void *v, int H, int L,
+                          int hidden, int D, float eps) {
   if (!x || !wq || !wk || !wv || !gamma_q || !gamma_k || !cos || !sin || !q || !k || !v) return H3_ERR_NULL;
-  if (!shape_ok(H, L) || hidden < 32 || hidden % 32 != 0 || hidden > (1 << 20) ||
+  if (fp8 && (!x_scale || !w_scale)) return H3_ERR_NULL;
+  const int step = fp8 ? 64 : 32;   // hidden elements per 64-byte step
+  if (!shape_ok(H, L) || hidden < step || hidden % step != 0 || hidden > (1 << 20) ||
       h3::qkv_proj_grid(H, L) >= (int64_t{1} << 31))
     return H3_ERR_SHAPE;
   if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
   const void *ptrs[] = {x, wq, wk, wv, gamma_q, gamma_k, cos, sin, q, k, v};
   for (const void *p : ptrs)
     if (!aligned16(p)) return H3_ERR_ALIGN;
+  if (fp8 && (!aligned4(x_scale) || !aligned4(w_scale))) return H3_ERR_ALIGN;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return H3_ERR_VALUE;
-  const uint64_t x_bytes = static_cast<uint64_t>(L) * hidden * 2;
-  const uint64_t w_bytes = static_cast<uint64_t>(H) * D * hidden * 2;
+  const uint64_t elem = fp8 ? 1 : 2;
+  const uint64_t x_bytes = static_cast<uint64_t>(L) * hidden * elem;
+  const uint64_t w_bytes = static_cast<uint64_t>(H) * D * hidden * elem;
   const uint64_t t_bytes = static_cast<uint64_t>(H) * L * D * 2;
   const uint64_t tab_bytes = static_cast<uint64_t>(L) * (D / 2) * 4;
   const void *outs[] = {q, k, v};
   const struct { const void *p; uint64_t n; } ins[] = {
-      {x, x_bytes}, {wq, w_bytes}, {wk, w_bytes}, {wv, w_bytes}, {gamma_q, D * 4u},
-      {gamma_k, D * 4u}, {cos, tab_bytes}, {sin, tab_bytes}};
+      {x, x_bytes}, {wq, w_bytes}, {wk, w_bytes}, {wv, w_bytes}, {gamma_q, D * 4u}, {gamma_k, D * 4u},
+      {cos, tab_bytes}, {sin, tab_bytes}, {x_scale, fp8 ? 4u : 0u}, {w_scale, fp8 ? 4u : 0u}};
   for (int i = 0; i < 3; ++i) {
     for (const auto &in : ins)
-      if (overlaps(outs[i], t_bytes, in.p, in.n)) return H3_ERR_ALIAS;
+      if (in.p && overlaps(outs[i], t_bytes, in.p, in.n)) return H3_ERR_ALIAS;
     for (int j = i + 1; j < 3; ++j)
       if (overlaps(outs[i], t_bytes, outs[j], t_bytes)) return H3_ERR_ALIAS;
   }
+  return H3_OK;
+}
+
+int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const void *wv,
+                            const float *gamma_q, const float *gamma_k, const float *cos,
+                            const float *sin, void *q, void *k, void *v, int H, int L,
+                            int hidden, int D, float eps, void *stream) {
+  const int st = check_qkv_proj(x, wq, wk, wv, nullptr, nullptr, false, gamma_q, gamma_k, cos, sin, q, k, v, H,
+                                L, hidden, D, eps);
+  if (st != H3_OK) return st;
   hipError_t e = h3::launch_qkv_proj_qknorm_rope(
       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wq), static_cast<const uint16_t *>(wk),
       static_cast<const uint16_t *>(wv), gamma_q, gamma_k, cos, sin, static_cast<uint16_t *>(q),
       static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+int h3_qkv_proj_fp8_qknorm_rope(const void *x, const float *x_scale, const void *wq, const void *wk,
+                                const void *wv, const float *w_scale, const float *gamma_q,
+                                const float *gamma_k, const float *cos, const float *sin, void *q,
+                                void *k, void *v, int H, int L, int hidden, int D, float eps,
+                                void *stream) {
+  const int st = check_qkv_proj(x, wq, wk, wv, x_scale, w_scale, true, gamma_q, gamma_k, cos, sin, q, k, v, H,
+                                L, hidden, D, eps);
+  if (st != H3_OK) return st;
+  hipError_t e = h3::launch_qkv_proj_fp8_qknorm_rope(
+      static_cast<const uint8_t *>(x), x_scale, static_cast<const uint8_t *>(wq),
+      static_cast<const uint8_t *>(wk), static_cast<const uint8_t *>(wv), w_scale, gamma_q, gamma_k, cos, sin,
+      static_cast<uint16_t *>(q), static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps,
       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }

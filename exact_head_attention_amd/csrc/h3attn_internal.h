@@ -38,4 +38,10 @@ hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, co
                                        const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k,
                                        uint16_t *v, int H, int L, int C, float eps, hipStream_t stream);
 
+hipError_t launch_qkv_proj_fp8_qknorm_rope(const uint8_t *x, const float *x_scale, const uint8_t *wq,
+                                           const uint8_t *wk, const uint8_t *wv, const float *w_scale,
+                                           const float *gamma_q, const float *gamma_k, const float *cos_t,
+                                           const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *v, int H, int L,
+                                           int C, float eps, hipStream_t stream);
+
 }  // namespace h3

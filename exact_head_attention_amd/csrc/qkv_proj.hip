@@ -19,10 +19,17 @@
 //     column and 16 features per lane, so a token's sum of squares over its
 //     128 features is lane-local plus one lane-half exchange, and each RoPE
 //     pair (2j, 2j+1) sits in one lane.
-//   * The hidden dimension streams in steps of 32 through double-buffered LDS
-//     (80-byte padded rows: 8 consecutive rows hit 8 disjoint bank groups);
-//     global loads are buffer loads one step ahead, so the last partial token
-//     tile reads zeros and writes nothing past L.
+//   * The hidden dimension streams in steps of 64 bytes per row (32 bf16 or
+//     64 fp8 elements) through double-buffered LDS (80-byte padded rows: 8
+//     consecutive rows hit 8 disjoint bank groups); global loads are buffer
+//     loads one step ahead, so the last partial token tile reads zeros and
+//     writes nothing past L.
+//   * fp8 form: OCP e4m3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+//     block scales), each lane's fragment 32 consecutive hidden elements of
+//     its row for both operands; any fixed split of a step's elements over
+//     lanes and registers pairs every element of A with the same element of
+//     B, so the dot product is complete.  The two per-tensor scales multiply
+//     the fp32 accumulator before the norm.
 //   * Blocks are ordered so that the 64 workgroups an XCD runs at once cover
 //     8 token tiles x 8 feature tiles: each hidden-state tile and each weight
 //     tile is then read by 8 concurrent workgroups through that XCD's L2.
@@ -38,14 +45,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = kHeadDim;          // features per head = per feature tile
 constexpr int kTok = 256;            // tokens per workgroup
 constexpr int kThreads = 256;        // 4 waves
-constexpr int kK = 32;               // hidden elements per LDS step
-constexpr int kStride = kK + 8;      // bf16 per LDS row (80 B)
-constexpr int kWChunks = D * (kK / 8) / kThreads;     // 16-byte chunks per thread per step: 2
-constexpr int kXChunks = kTok * (kK / 8) / kThreads;  // 4
+constexpr int kStepBytes = 64;      // bytes of each row per LDS step
+constexpr int kStride = 40;          // uint16 slots per LDS row (80 B)
+constexpr int kWChunks = D * (kStepBytes / 16) / kThreads;     // 16-byte chunks per thread per step: 2
+constexpr int kXChunks = kTok * (kStepBytes / 16) / kThreads;  // 4
+constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
 
@@ -73,9 +82,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
 }
 
+// kFp8 = false: bf16 operands.  kFp8 = true: e4m3 operands with per-tensor
+// scales *x_scale and *w_scale (device scalars).  C counts hidden elements.
+template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
-    const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wq, const uint16_t *__restrict__ Wk,
-    const uint16_t *__restrict__ Wv, const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
+    const uint8_t *__restrict__ X, const uint8_t *__restrict__ Wq, const uint8_t *__restrict__ Wk,
+    const uint8_t *__restrict__ Wv, const float *__restrict__ x_scale, const float *__restrict__ w_scale,
+    const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
   __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][D * kStride];
@@ -98,17 +111,17 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   const int head = ft - which * H;
   const int t0 = tt * kTok;
 
-  const uint16_t *Wsel = which == 0 ? Wq : which == 1 ? Wk : Wv;
-  const int row_bytes = C * 2;
+  const uint8_t *Wsel = which == 0 ? Wq : which == 1 ? Wk : Wv;
+  const int row_bytes = C * (kFp8 ? 1 : 2);
   const int tok_rows = L - t0 < kTok ? L - t0 : kTok;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wsel + static_cast<size_t>(head) * D * C, D * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * C, tok_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wsel + static_cast<size_t>(head) * D * row_bytes, D * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * row_bytes, tok_rows * row_bytes);
 
   // Staging: chunk c = tid + 256 i of a step covers row c/4, bytes 16 (c%4)
   // of the step's 64-byte slice of that row.
   uint4 sw[kWChunks], sx[kXChunks];
   auto load = [&](int ks) {
-    const uint32_t kb = static_cast<uint32_t>(ks) * kK * 2;
+    const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
 #pragma unroll
     for (int i = 0; i < kWChunks; ++i) {
       const int c = tid + kThreads * i;
@@ -139,20 +152,39 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
 #pragma unroll
     for (int ts = 0; ts < 2; ++ts) acc[fs][ts] = f32x16{};
 
-  const int n_k = C / kK;
+  const int n_k = row_bytes / kStepBytes;
   load(0);
   store(0);
   if (n_k > 1) load(1);
   __syncthreads();
 
-  // Fragment addresses: A = weight row 32fs + l32, B = token row 64w + 32ts + l32,
-  // both at hidden offset 16kk + 8g within the step.
-  const uint16_t *wa = &w_lds[0][l32 * kStride + 8 * g];
-  const uint16_t *xb = &x_lds[0][(wave * 64 + l32) * kStride + 8 * g];
+  // Fragment addresses: A = weight row 32fs + l32, B = token row 64w + 32ts +
+  // l32; bf16: bytes 32kk + 16g of the step's 64, fp8: bytes 32g .. 32g+31.
+  const uint16_t *wa = &w_lds[0][l32 * kStride + (kFp8 ? 16 : 8) * g];
+  const uint16_t *xb = &x_lds[0][(wave * 64 + l32) * kStride + (kFp8 ? 16 : 8) * g];
+  auto frag32 = [](const uint16_t *p) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(p);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(p + 8);
+    return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  };
   for (int ks = 0; ks < n_k; ++ks) {
     const int buf = ks & 1;
+    if constexpr (kFp8) {
+      i32x8 a[4], b[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int fs = 0; fs < 4; ++fs) a[fs] = frag32(wa + buf * (D * kStride) + fs * 32 * kStride);
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) b[ts] = frag32(xb + buf * (kTok * kStride) + ts * 32 * kStride);
+#pragma unroll
+      for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+          acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
+                                                                        kE8M0One, 0, kE8M0One);
+    }
+#pragma unroll
+    for (int kk = 0; kk < (kFp8 ? 0 : 2); ++kk) {
       bf16x8 a[4], b[2];
 #pragma unroll
       for (int fs = 0; fs < 4; ++fs)
@@ -179,6 +211,13 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   // t0 + 64w + 32ts + l32.
   uint16_t *Out = which == 0 ? Qo : which == 1 ? Ko : Vo;
   const float *gamma = which == 0 ? gamma_q : gamma_k;
+  if constexpr (kFp8) {
+    const float sc = x_scale[0] * w_scale[0];
+#pragma unroll
+    for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) acc[fs][ts] *= sc;
+  }
 #pragma unroll
   for (int ts = 0; ts < 2; ++ts) {
     const int t = t0 + wave * 64 + ts * 32 + l32;
@@ -231,8 +270,22 @@ hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, co
                                        uint16_t *v, int H, int L, int C, float eps, hipStream_t stream) {
   const int n_ttiles = (L + kTok - 1) / kTok;
   const int blocks = static_cast<int>(qkv_proj_grid(H, L));
-  hipLaunchKernelGGL(qkv_proj_kernel, dim3(blocks), dim3(kThreads), 0, stream, x, wq, wk, wv, gamma_q, gamma_k,
-                     cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
+  hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(wq),
+                     reinterpret_cast<const uint8_t *>(wk), reinterpret_cast<const uint8_t *>(wv), nullptr, nullptr,
+                     gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_fp8_qknorm_rope(const uint8_t *x, const float *x_scale, const uint8_t *wq,
+                                           const uint8_t *wk, const uint8_t *wv, const float *w_scale,
+                                           const float *gamma_q, const float *gamma_k, const float *cos_t,
+                                           const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *v, int H, int L,
+                                           int C, float eps, hipStream_t stream) {
+  const int n_ttiles = (L + kTok - 1) / kTok;
+  const int blocks = static_cast<int>(qkv_proj_grid(H, L));
+  hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, x, wq, wk, wv, x_scale,
+                     w_scale, gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
   return hipGetLastError();
 }
 

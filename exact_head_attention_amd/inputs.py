@@ -33,9 +33,15 @@ state, H3's hidden size 5376; "buqi-minimax-h3-multigpu", How it works):
   proj_ws8     H=7,  L=32768, hidden=5376  (31744 video + 1024 audio)
   proj_ws2     H=28, L=32768, hidden=5376  (the all_gather form's world_size 2)
 
+  proj8_ws8    the fp8 form of proj_ws8;   proj8_ws2  the fp8 form of proj_ws2
+
 Draw order from Generator(PCG64(seed)): x (standard normal), then wq, wk, wv
 (standard normal / sqrt(hidden), so each projected feature is about N(0,1)),
 each rounded to bf16; then gamma_q and gamma_k (1 + 0.1 * standard normal).
+The fp8 forms draw the same fp32 values and quantise them instead: x with
+x_scale = max|x| / 448, the three weight slices with one w_scale = max over
+all three / 448 (one scale per tensor), each value / scale rounded to e4m3 by
+PyTorch's float8_e4m3fn conversion (data preparation, not the method).
 """
 from __future__ import annotations
 
@@ -88,6 +94,7 @@ class ProjWorkload:
     n_video: int
     n_audio: int
     hidden: int
+    fp8: bool = False
     D: int = HEAD_DIM
 
     @property
@@ -101,18 +108,38 @@ PROJ_WORKLOADS = {
     "proj_tiny": ProjWorkload("proj_tiny", H=2, L=300, n_video=256, n_audio=44, hidden=512),
     "proj_ws8": ProjWorkload("proj_ws8", H=7, L=32768, n_video=31744, n_audio=1024, hidden=5376),
     "proj_ws2": ProjWorkload("proj_ws2", H=28, L=32768, n_video=31744, n_audio=1024, hidden=5376),
+    "proj8_ws8": ProjWorkload("proj8_ws8", H=7, L=32768, n_video=31744, n_audio=1024, hidden=5376, fp8=True),
+    "proj8_ws2": ProjWorkload("proj8_ws2", H=28, L=32768, n_video=31744, n_audio=1024, hidden=5376, fp8=True),
 }
+
+
+def _to_e4m3_bits(x: np.ndarray, scale: float) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x / np.float32(scale), dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def make_proj_inputs(w: ProjWorkload, seed: int = 0) -> dict:
     """Hidden state, weight slices, gammas and positions of a projection
-    workload.  x: uint16 bf16 bits [L, hidden]; wq, wk, wv: bits [H*D, hidden];
+    workload.  x: uint16 bf16 bits [L, hidden]; wq, wk, wv: bits [H*D, hidden]
+    (fp8 forms: uint8 e4m3 codes, plus fp32 x_scale and w_scale);
     gamma_q, gamma_k fp32 [D]; positions int32 [L]; eps and theta."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    out = {"x": f32_to_bf16_bits(rng.standard_normal((w.L, w.hidden), dtype=np.float32))}
+    xf = rng.standard_normal((w.L, w.hidden), dtype=np.float32)
     wscale = np.float32(1.0 / math.sqrt(w.hidden))
-    for name in ("wq", "wk", "wv"):
-        out[name] = f32_to_bf16_bits(rng.standard_normal((w.H * w.D, w.hidden), dtype=np.float32) * wscale)
+    wf = {n: rng.standard_normal((w.H * w.D, w.hidden), dtype=np.float32) * wscale for n in ("wq", "wk", "wv")}
+    out = {}
+    if w.fp8:
+        out["x_scale"] = np.float32(np.abs(xf).max() / 448.0)
+        out["w_scale"] = np.float32(max(float(np.abs(a).max()) for a in wf.values()) / 448.0)
+        out["x"] = _to_e4m3_bits(xf, out["x_scale"])
+        for name, a in wf.items():
+            out[name] = _to_e4m3_bits(a, out["w_scale"])
+    else:
+        out["x"] = f32_to_bf16_bits(xf)
+        for name, a in wf.items():
+            out[name] = f32_to_bf16_bits(a)
+    del xf, wf
     out["gamma_q"] = (1.0 + 0.1 * rng.standard_normal(w.D, dtype=np.float32)).astype(np.float32)
     out["gamma_k"] = (1.0 + 0.1 * rng.standard_normal(w.D, dtype=np.float32)).astype(np.float32)
     out["positions"] = packed_positions(w.n_video, w.n_audio)

@@ -184,6 +184,32 @@ int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const
                             const float *sin, void *q, void *k, void *v, int H, int L,
                             int hidden, int D, float eps, void *stream);
 
+/*
+ * The fp8 form of h3_qkv_proj_qknorm_rope.  The checkpoint the page
+ * recommends stores fp8 weights with one scale per tensor, and its
+ * transformer GEMMs run in fp8 ("buqi-minimax-h3-multigpu", VRAM & resolution
+ * guidance and How it works).  Both operands are OCP e4m3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits):
+ *   q~[h][t][d] = x_scale * w_scale * sum_c x[t][c] * wq[h*D+d][c]
+ * (k~, v~ likewise), then the same norm, rotation and bf16 rounding as the
+ * bf16 form.  Products on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4
+ * with unit block scales), fp32 accumulation; the scales multiply the fp32
+ * accumulator before the norm.
+ *
+ *   x             e4m3 [L][hidden];   x_scale  fp32 scalar in device memory.
+ *   wq, wk, wv    e4m3 [H*D][hidden]: row slices of one weight tensor;
+ *                 w_scale  its fp32 scale, a scalar in device memory.
+ *   the rest      as for h3_qkv_proj_qknorm_rope; hidden a positive multiple
+ *                 of 64, at most 2^20.
+ * x, w*, gamma, cos, sin, q, k, v must be 16-byte aligned, the scales 4-byte
+ * aligned.  Scales are read on the device, so the call needs no host sync.
+ */
+int h3_qkv_proj_fp8_qknorm_rope(const void *x, const float *x_scale, const void *wq, const void *wk,
+                                const void *wv, const float *w_scale, const float *gamma_q,
+                                const float *gamma_k, const float *cos, const float *sin, void *q,
+                                void *k, void *v, int H, int L, int hidden, int D, float eps,
+                                void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *h3_status_string(int status);
 

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
-              "h3_qkv_proj_qknorm_rope", "h3_status_string", "h3_abi_version"):
+              "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope", "h3_status_string", "h3_abi_version"):
         assert n in names
 
 
@@ -150,3 +150,19 @@ def test_qkv_proj_argument_errors(B):
     assert _qkv(B, k=A + 8 * MB + 64) == -5                # k inside q
     assert _qkv(B, q=A + 6 * MB) == -5                     # q over cos
     assert _qkv(B, eps=0.0) == -6 and _qkv(B, eps=float("inf")) == -6
+
+
+def _qkv8(B, x=A, xs=A + 11 * MB, wq=A + 1 * MB, wk=A + 2 * MB, wv=A + 3 * MB, ws=A + 11 * MB + 64,
+          gq=A + 4 * MB, gk=A + 5 * MB, c=A + 6 * MB, s=A + 7 * MB, q=A + 8 * MB, k=A + 9 * MB, v=A + 10 * MB,
+          H=2, L=512, C=256, D=128, eps=1e-6):
+    return B.lib.h3_qkv_proj_fp8_qknorm_rope(x, xs, wq, wk, wv, ws, gq, gk, c, s, q, k, v, H, L, C, D, eps, None)
+
+
+def test_qkv_proj_fp8_argument_errors(B):
+    assert _qkv8(B, xs=None) == -1 and _qkv8(B, ws=None) == -1 and _qkv8(B, x=None) == -1
+    assert _qkv8(B, C=32) == -2 and _qkv8(B, C=96) == -2 and _qkv8(B, L=0) == -2
+    assert _qkv8(B, D=256) == -3
+    assert _qkv8(B, xs=A + 11 * MB + 2) == -4 and _qkv8(B, wq=A + 1 * MB + 8) == -4
+    assert _qkv8(B, q=A + 11 * MB - 16) == -5               # q's end covers x_scale
+    assert _qkv8(B, v=A + 10 * MB, k=A + 10 * MB + 4096) == -5
+    assert _qkv8(B, eps=-1.0) == -6

@@ -62,3 +62,16 @@ def test_projection_inputs():
     assert not np.array_equal(a["wq"], a["wk"])
     assert I.PROJ_WORKLOADS["proj_ws2"].hidden == 5376 and I.PROJ_WORKLOADS["proj_ws2"].H == 28
     assert I.PROJ_WORKLOADS["proj_ws2"].flops == 2.0 * 32768 * 3 * 28 * 128 * 5376
+
+
+def test_projection_fp8_inputs():
+    w = I.ProjWorkload("t8", H=1, L=64, n_video=64, n_audio=0, hidden=128, fp8=True)
+    a = I.make_proj_inputs(w, seed=3)
+    assert a["x"].dtype == np.uint8 and a["wq"].shape == (128, 128)
+    import torch
+    x = torch.from_numpy(a["x"]).view(torch.float8_e4m3fn).float().numpy() * a["x_scale"]
+    assert abs(float(np.abs(x).max()) - 448.0 * float(a["x_scale"])) < 1e-6 * 448.0 * float(a["x_scale"]) * 4
+    assert abs(float(x.std()) - 1.0) < 0.1
+    b = I.make_proj_inputs(I.ProjWorkload("t16", H=1, L=64, n_video=64, n_audio=0, hidden=128), seed=3)
+    xb = (b["x"].astype(np.uint32) << 16).view(np.float32)
+    assert np.corrcoef(xb.ravel(), x.ravel())[0, 1] > 0.99   # same draws, two encodings
