@@ -75,7 +75,8 @@ def summarize(args):
                                                   recursive=True)[0])))
         out.append(f"# rocprofv3 --kernel-trace --stats, workload {args.workload}")
         out.append(f"# command: {args.command}")
-        out.append(f"# attn_fwd.hip sha256[:16] = {source_digest()}")
+        src = args.source or ATTN_SOURCE
+        out.append(f"# {os.path.basename(src)} sha256[:16] = {source_digest(src)}")
         out.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
         call_us = 0.0
         for r in rows:
@@ -87,11 +88,13 @@ def summarize(args):
             elif "FillFunctor" in r["Name"] or "fillBuffer" in r["Name"]:
                 name = "torch fill"
             elif "copyBuffer" in r["Name"]:
-                name = "device copies (largest = 512 MiB calibration)"
+                name = ("device copies (largest = 512 MiB calibration)" if float(r["MaxNs"]) > 1e5
+                        else "device copies (small uploads)")
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
-        out.append(f"# one h3_attention call = attn_fwd_kernel<8, false> (full rounds) + attn_fwd_kernel<4, false> "
-                   f"(tail, when launched): {call_us:.2f} us per call")
+        if call_us > 0:
+            out.append(f"# one h3_attention call = attn_fwd_kernel<8, false> (full rounds) + "
+                       f"attn_fwd_kernel<4, false> (tail, when launched): {call_us:.2f} us per call")
     if args.pmc:
         per = {}
         for d in args.pmc:
@@ -245,6 +248,7 @@ def main():
     ap.add_argument("--kernel-stats", default=None)
     ap.add_argument("--pmc", nargs="*", default=None)
     ap.add_argument("--command", default="")
+    ap.add_argument("--source", default=None, help="kernel source whose hash the summary records")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)

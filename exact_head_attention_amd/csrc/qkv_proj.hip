@@ -10,8 +10,10 @@
 // the norm.  Outputs are [H][L][128] bf16, the layout the attention reads.
 //
 // Work decomposition
-//   * Workgroup = (feature tile, token tile): 128 output features (one head
-//     of q, k or v) x 256 tokens; 4 waves, each 128 features x 64 tokens.
+//   * Workgroup = (feature tile, token tile): two head slots (256 output
+//     features; slot j of the 3H q, k, v heads) x 256 tokens; 4 waves, each
+//     one head slot (128 features) x 128 tokens, with its 16 accumulator
+//     tiles (256 registers) in AGPRs: one wave per SIMD.
 //   * The product is computed transposed, C^T = W . X^T, with
 //     v_mfma_f32_32x32x16_bf16: A = weight rows (features), B = hidden rows
 //     (tokens).  Both operands are K-contiguous in memory, so every fragment
@@ -30,9 +32,10 @@
 //     lanes and registers pairs every element of A with the same element of
 //     B, so the dot product is complete.  The two per-tensor scales multiply
 //     the fp32 accumulator before the norm.
-//   * Blocks are ordered so that the 64 workgroups an XCD runs at once cover
-//     8 token tiles x 8 feature tiles: each hidden-state tile and each weight
-//     tile is then read by 8 concurrent workgroups through that XCD's L2.
+//   * Blocks are ordered so that the workgroups an XCD runs at once cover
+//     8 token tiles x 4 feature tiles: each hidden-state tile and each weight
+//     tile is then read by several concurrent workgroups through that XCD's
+//     L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,16 +50,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int D = kHeadDim;          // features per head = per feature tile
+constexpr int D = kHeadDim;          // features per head slot
+constexpr int kSlots = 2;            // head slots (of the 3H q, k, v heads) per workgroup
 constexpr int kTok = 256;            // tokens per workgroup
-constexpr int kThreads = 256;        // 4 waves
-constexpr int kStepBytes = 64;      // bytes of each row per LDS step
+constexpr int kThreads = 256;        // 4 waves: (slot, token half)
+constexpr int kStepBytes = 64;       // bytes of each row per LDS step
 constexpr int kStride = 40;          // uint16 slots per LDS row (80 B)
-constexpr int kWChunks = D * (kStepBytes / 16) / kThreads;     // 16-byte chunks per thread per step: 2
-constexpr int kXChunks = kTok * (kStepBytes / 16) / kThreads;  // 4
-constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
+constexpr int kRows = kSlots * D;    // weight rows per workgroup
+constexpr int kWChunks = kRows * (kStepBytes / 16) / kThreads;   // 16-byte chunks per thread per step: 4
+constexpr int kXChunks = kTok * (kStepBytes / 16) / kThreads;    // 4
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
+constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
@@ -84,14 +89,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 
 // kFp8 = false: bf16 operands.  kFp8 = true: e4m3 operands with per-tensor
 // scales *x_scale and *w_scale (device scalars).  C counts hidden elements.
+// Head slot j in [0, 3H) is q head j, k head j - H or v head j - 2H.
 template <bool kFp8>
-__global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
+__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ Wq, const uint8_t *__restrict__ Wk,
     const uint8_t *__restrict__ Wv, const float *__restrict__ x_scale, const float *__restrict__ w_scale,
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][D * kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][kRows * kStride];
   __shared__ __attribute__((aligned(16))) uint16_t x_lds[2][kTok * kStride];
 
   const int tid = threadIdx.x;
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   const int l32 = lane & 31, g = lane >> 5;
 
   // logical -> (token group, feature tile, token tile within the group)
-  const int n_ft = 3 * H;
+  const int n_ft = (3 * H + kSlots - 1) / kSlots;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = kGroupTiles * n_ft;
   const int tg = logical / per_group;
@@ -107,25 +113,33 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   const int gsz = min(kGroupTiles, n_ttiles - tg * kGroupTiles);
   const int ft = rem / gsz;
   const int tt = tg * kGroupTiles + (rem - ft * gsz);
-  const int which = ft / H;          // 0 q, 1 k, 2 v
-  const int head = ft - which * H;
   const int t0 = tt * kTok;
 
-  const uint8_t *Wsel = which == 0 ? Wq : which == 1 ? Wk : Wv;
   const int row_bytes = C * (kFp8 ? 1 : 2);
   const int tok_rows = L - t0 < kTok ? L - t0 : kTok;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wsel + static_cast<size_t>(head) * D * row_bytes, D * row_bytes);
+  // One descriptor per slot; a slot past 3H (odd 3H) reads zeros.
+  __amdgpu_buffer_rsrc_t rw[kSlots];
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl) {
+    const int j = ft * kSlots + sl;
+    const int wh = j / H, hd = j - (j / H) * H;
+    const uint8_t *base = wh == 0 ? Wq : wh == 1 ? Wk : Wv;
+    rw[sl] = make_rsrc(base + static_cast<size_t>(wh < 3 ? hd : 0) * D * row_bytes, j < 3 * H ? D * row_bytes : 0);
+  }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * row_bytes, tok_rows * row_bytes);
 
-  // Staging: chunk c = tid + 256 i of a step covers row c/4, bytes 16 (c%4)
-  // of the step's 64-byte slice of that row.
+  // Staging: chunk c = tid + 256 i of a step covers row c/4 (weight rows
+  // 0..255 over the two slots, or token rows), bytes 16 (c%4) of the step's
+  // 64-byte slice of that row.
   uint4 sw[kWChunks], sx[kXChunks];
   auto load = [&](int ks) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
 #pragma unroll
     for (int i = 0; i < kWChunks; ++i) {
-      const int c = tid + kThreads * i;
-      sw[i] = bload128(rw, (c >> 2) * row_bytes + kb + 16 * (c & 3));
+      // Chunks i = 0, 1 are slot 0's rows 0..127, i = 2, 3 slot 1's.
+      constexpr int kPerSlot = kWChunks / kSlots;
+      const int row = (tid >> 2) + (kThreads / 4) * (i % kPerSlot);
+      sw[i] = bload128(rw[i / kPerSlot], row * row_bytes + kb + 16 * (tid & 3));
     }
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) {
@@ -146,11 +160,13 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
     }
   };
 
-  f32x16 acc[4][2];
+  // Wave (sl, th): head slot sl of the tile, tokens 128 th .. 128 th + 127.
+  const int sl = wave & 1, th = wave >> 1;
+  f32x16 acc[4][4];
 #pragma unroll
   for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts) acc[fs][ts] = f32x16{};
+    for (int ts = 0; ts < 4; ++ts) acc[fs][ts] = f32x16{};
 
   const int n_k = row_bytes / kStepBytes;
   load(0);
@@ -158,10 +174,11 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   if (n_k > 1) load(1);
   __syncthreads();
 
-  // Fragment addresses: A = weight row 32fs + l32, B = token row 64w + 32ts +
-  // l32; bf16: bytes 32kk + 16g of the step's 64, fp8: bytes 32g .. 32g+31.
-  const uint16_t *wa = &w_lds[0][l32 * kStride + (kFp8 ? 16 : 8) * g];
-  const uint16_t *xb = &x_lds[0][(wave * 64 + l32) * kStride + (kFp8 ? 16 : 8) * g];
+  // Fragment addresses: A = weight row 128 sl + 32 fs + l32, B = token row
+  // 128 th + 32 ts + l32; bf16: bytes 32kk + 16g of the step's 64, fp8: bytes
+  // 32g .. 32g+31.
+  const uint16_t *wa = &w_lds[0][(sl * D + l32) * kStride + (kFp8 ? 16 : 8) * g];
+  const uint16_t *xb = &x_lds[0][(th * 128 + l32) * kStride + (kFp8 ? 16 : 8) * g];
   auto frag32 = [](const uint16_t *p) {
     const uint4 lo = *reinterpret_cast<const uint4 *>(p);
     const uint4 hi = *reinterpret_cast<const uint4 *>(p + 8);
@@ -170,33 +187,36 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
   };
   for (int ks = 0; ks < n_k; ++ks) {
     const int buf = ks & 1;
+    const uint16_t *wab = wa + buf * (kRows * kStride);
+    const uint16_t *xbb = xb + buf * (kTok * kStride);
     if constexpr (kFp8) {
-      i32x8 a[4], b[2];
+      i32x8 a[4], b[4];
 #pragma unroll
-      for (int fs = 0; fs < 4; ++fs) a[fs] = frag32(wa + buf * (D * kStride) + fs * 32 * kStride);
-#pragma unroll
-      for (int ts = 0; ts < 2; ++ts) b[ts] = frag32(xb + buf * (kTok * kStride) + ts * 32 * kStride);
+      for (int i = 0; i < 4; ++i) {
+        a[i] = frag32(wab + i * 32 * kStride);
+        b[i] = frag32(xbb + i * 32 * kStride);
+      }
 #pragma unroll
       for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
+        for (int ts = 0; ts < 4; ++ts)
           acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
                                                                         kE8M0One, 0, kE8M0One);
-    }
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < (kFp8 ? 0 : 2); ++kk) {
-      bf16x8 a[4], b[2];
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 a[4], b[4];
 #pragma unroll
-      for (int fs = 0; fs < 4; ++fs)
-        a[fs] = *reinterpret_cast<const bf16x8 *>(wa + buf * (D * kStride) + fs * 32 * kStride + 16 * kk);
+        for (int i = 0; i < 4; ++i) {
+          a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kStride + 16 * kk);
+          b[i] = *reinterpret_cast<const bf16x8 *>(xbb + i * 32 * kStride + 16 * kk);
+        }
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts)
-        b[ts] = *reinterpret_cast<const bf16x8 *>(xb + buf * (kTok * kStride) + ts * 32 * kStride + 16 * kk);
+        for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-      for (int fs = 0; fs < 4; ++fs)
-#pragma unroll
-        for (int ts = 0; ts < 2; ++ts)
-          acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
+          for (int ts = 0; ts < 4; ++ts)
+            acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
+      }
     }
     if (ks + 1 < n_k) {
       // Buffer buf^1 was last read in step ks-1, before the barrier that
@@ -207,8 +227,11 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
     __syncthreads();
   }
 
-  // Epilogue.  acc[fs][ts][i] = feature 32fs + 8(i/4) + 4g + i%4 of token
-  // t0 + 64w + 32ts + l32.
+  // Epilogue.  acc[fs][ts][i] = feature 32fs + 8(i/4) + 4g + i%4 of the
+  // wave's head slot, token t0 + 128 th + 32 ts + l32.
+  const int j = ft * kSlots + sl;
+  if (j >= 3 * H) return;
+  const int which = j / H, head = j - which * H;   // 0 q, 1 k, 2 v
   uint16_t *Out = which == 0 ? Qo : which == 1 ? Ko : Vo;
   const float *gamma = which == 0 ? gamma_q : gamma_k;
   if constexpr (kFp8) {
@@ -216,11 +239,11 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
 #pragma unroll
     for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts) acc[fs][ts] *= sc;
+      for (int ts = 0; ts < 4; ++ts) acc[fs][ts] *= sc;
   }
 #pragma unroll
-  for (int ts = 0; ts < 2; ++ts) {
-    const int t = t0 + wave * 64 + ts * 32 + l32;
+  for (int ts = 0; ts < 4; ++ts) {
+    const int t = t0 + th * 128 + ts * 32 + l32;
     float r = 1.0f;
     if (which < 2) {
       float ss = 0.f;
@@ -261,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_proj_kernel(
 }  // namespace
 
 int64_t qkv_proj_grid(int H, int L) {
-  return static_cast<int64_t>(3) * H * ((static_cast<int64_t>(L) + kTok - 1) / kTok);
+  return ((static_cast<int64_t>(3) * H + kSlots - 1) / kSlots) * ((static_cast<int64_t>(L) + kTok - 1) / kTok);
 }
 
 hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, const uint16_t *wk,
