@@ -188,3 +188,37 @@ def test_attention_ws1_sampled_and_head_splits(gpu_lib):
         for h in range(56):
             assert torch.equal(split[h], full[h]), f"head {h} differs with {chunk}-head launches"
         del split
+
+
+@pytest.mark.timeout(600)
+def test_attention_max_length(gpu_lib):
+    """L = 2^23, the longest sequence the ABI accepts (H = 1).  Keys and values
+    are 65536 seeded rows repeated 128 times: repeating every key m times
+    leaves the softmax weights unchanged, so the oracle over the distinct rows
+    is the exact answer while the GPU runs the full-length path.  Queries are
+    8192 seeded rows tiled over the sequence; a row's arithmetic depends only
+    on its values, so every copy of a query row must give the same bits."""
+    import sys
+    import torch
+    L, kv_base, q_base = 1 << 23, 1 << 16, 1 << 13
+    rng = np.random.Generator(np.random.PCG64(2023))
+    qb = I.f32_to_bf16_bits(rng.standard_normal((q_base, 128), dtype=np.float32))
+    kb = I.f32_to_bf16_bits(rng.standard_normal((kv_base, 128), dtype=np.float32))
+    vb = I.f32_to_bf16_bits(rng.standard_normal((kv_base, 128), dtype=np.float32))
+    q = to_dev(qb, torch.bfloat16).repeat(L // q_base, 1).view(1, L, 128)
+    k = to_dev(kb, torch.bfloat16).repeat(L // kv_base, 1).view(1, L, 128)
+    v = to_dev(vb, torch.bfloat16).repeat(L // kv_base, 1).view(1, L, 128)
+    print("max-length attention: H=1 L=2^23 launch", flush=True)
+    sys.stdout.flush()
+    out = gpu_lib.attention(q, k, v, scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    print("max-length attention: done", flush=True)
+    blocks = out.view(L // q_base, q_base, 128)
+    assert torch.equal(blocks, blocks[:1].expand_as(blocks)), "copies of one query row differ"
+    rows = np.unique(np.concatenate([[0, q_base - 1], rng.choice(q_base, 62, replace=False)]))
+    ref = oracle.attention_head(oracle.bf16_to_f64(qb[rows]), oracle.bf16_to_f64(kb), oracle.bf16_to_f64(vb),
+                                1 / math.sqrt(128))
+    err = row_rel_err(bits(out[0, :q_base])[rows], ref)
+    last = row_rel_err(bits(out[0, L - q_base:])[rows], ref)
+    print(f"L=2^23: max row rel err {max(err.max(), last.max()):.3e}")
+    assert err.max() <= ATTN_TOL and last.max() <= ATTN_TOL
