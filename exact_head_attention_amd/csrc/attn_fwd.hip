@@ -235,6 +235,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     return *reinterpret_cast<const bf16x8 *>(kp + b * 32 * kKStride + 16 * c);
   };
 
+  // Mask the keys of tile t at or past Lk (only the last, ragged tile has any).
+  // s[b][i] holds key t*64 + 32b + 16(i/8) + 8g + i%8.
+  auto mask_tile = [&](f32x16 (&sv)[2], int t) {
+    const int key_base = t * kBc;
+    if (key_base + kBc > Lk) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= Lk) sv[b][i] = -__builtin_inff();
+    }
+  };
+
   f32x16 s_a[2], s_b[2];
   {
     s_a[0] = f32x16{};
@@ -245,25 +258,27 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kfrag, 1, c), qf[c], s_a[1], 0, 0, 0);
     }
   }
+  mask_tile(s_a, 0);
+  // Row max (scaled, base 2) of the tile whose softmax the next step does.
+  float mx = lane_half_max(max32(s_a[0], s_a[1])) * scale_log2e;
 
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  // One key tile: softmax of s_cur (tile kt), scores of tile kt+1 into s_nxt,
-  // O += P.V for tile kt, then LDS staging of K tile kt+2 and V tile kt+1
-  // from st_store while st_load fetches K tile kt+3 and V tile kt+2.
+  // One key tile.  Everything that does not feed the matrix cores runs in
+  // their shadow, so the two waves sharing a SIMD (kept in step by the
+  // barrier) leave the matrix pipe idle only around that barrier:
+  //   (1) raise the running max if tile kt's max (found last step) exceeds it;
+  //   (2) scores of tile kt+1 on the matrix cores, interleaved with tile kt's
+  //       exponentials, with V tile kt+1 staged to LDS and the global loads
+  //       of K tile kt+3 and V tile kt+2 issued in between;
+  //   (3) O += P.V for tile kt, interleaved with tile kt+1's row max and the
+  //       LDS staging of K tile kt+2.
+  // The staged buffers are free: K tile kt's buffer was last read for the
+  // scores of tile kt (the previous step) and V tile kt-1's for the previous
+  // step's P.V, both before the barrier that ended it.
   auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 *st_store, uint4 *st_load) {
-    // (1) Mask the ragged tail, row max, and (rarely) raise the running max.
-    // s_cur[b][i] holds key kt*64 + 32b + 16(i/8) + 8g + i%8.
-    const int key_base = kt * kBc;
-    if (key_base + kBc > Lk) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= Lk) s_cur[b][i] = -__builtin_inff();
-    }
-    const float mxs = lane_half_max(max32(s_cur[0], s_cur[1])) * scale_log2e;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_run) != 0) {
-      const float m_new = __builtin_fmaxf(m_run, mxs);
+    // (1)
+    if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run0 *= alpha;
@@ -275,23 +290,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
     const float neg_m = -m_run;
 
+    // (2) K fragments are read one MFMA pair ahead (ping-pong registers).
+    store_rows(v_lds[(kt + 1) & 1], kVStride, vpart(st_store));
     load_kv(Kh, kt + 3, kpart(st_load));
     load_kv(Vh, kt + 2, vpart(st_load));
-
-    // (2) Scores of tile kt+1 on the matrix cores, interleaved step by step
-    // with the exponentials of tile kt on the vector ALUs; K fragments are
-    // read one step ahead.
     const uint16_t *kp = kfrag + ((kt + 1) & 1) * (kBc * kKStride);
     uint32_t pw[16];
-    bf16x8 a0 = kread(kp, 0, 0), a1 = kread(kp, 1, 0);
+    bf16x8 ka[2][2];
+    ka[0][0] = kread(kp, 0, 0);
+    ka[0][1] = kread(kp, 1, 0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      bf16x8 n0 = a0, n1 = a1;
+      const int cur = c & 1, nxt = cur ^ 1;
       if (c < 7) {
-        n0 = kread(kp, 0, c + 1);
-        n1 = kread(kp, 1, c + 1);
+        ka[nxt][0] = kread(kp, 0, c + 1);
+        ka[nxt][1] = kread(kp, 1, c + 1);
       }
-      s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
+      s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int b = c >> 2, i = 4 * (c & 3) + 2 * e;
@@ -303,43 +318,46 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         else
           l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run1, false);
       }
-      s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
-      a0 = n0;
-      a1 = n1;
-      if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next step's 2 LDS reads
+      s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][1], qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
+      if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's 2 LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+      if (c == 0) __builtin_amdgcn_sched_group_barrier(0x200, kChunks, 0);   // V staging writes
+      if (c == 1 || c == 2) __builtin_amdgcn_sched_group_barrier(0x020, kChunks, 0);   // global loads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
     }
 
-    // (3) O^T += V_tile^T . P^T.  pw[4*(2b+t) + 0..3] holds the bf16 weights
-    // of keys 32b + 16t + 8g + 0..7, the same keys the transposed V reads
-    // deliver for k-step bt = 2b + t.  V fragments are read one k-step ahead.
+    // (3) pw[4*(2b+t) + 0..3] holds the bf16 weights of keys 32b + 16t + 8g
+    // + 0..7, the same keys the transposed V reads deliver for k-step
+    // bt = 2b + t.  V fragments are read one k-step ahead (ping-pong).
+    mask_tile(s_nxt, kt + 1);
     const uint16_t *vp = vfrag + (kt & 1) * (kBc * kVStride);
-    bf16x8 vf[4];
+    bf16x8 vf[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vf[db] = vread(vp + 32 * db);
+    for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp + 32 * db);
+    store_rows(k_lds[kt & 1], kKStride, kpart(st_store));
+    const float mx_next = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
-      bf16x8 vn[4];
+      const int cur = bt & 1, nxt = cur ^ 1;
       if (bt < 3) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vn[db] = vread(vp + (16 * (bt + 1)) * kVStride + 32 * db);
+        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp + (16 * (bt + 1)) * kVStride + 32 * db);
       }
       const uint4 w = make_uint4(pw[4 * bt], pw[4 * bt + 1], pw[4 * bt + 2], pw[4 * bt + 3]);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], __builtin_bit_cast(bf16x8, w), o[db], 0, 0, 0);
-      if (bt < 3) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], __builtin_bit_cast(bf16x8, w), o[db], 0, 0, 0);
+      if (bt < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next k-step's V reads
+      if (bt == 0) __builtin_amdgcn_sched_group_barrier(0x200, kChunks, 0);   // K staging writes
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[db] = vn[db];
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next k-step's V reads
+      for (int m = 0; m < 4; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);           // VALU (the max tree)
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);     // 4 MFMAs
     }
-    store_rows(k_lds[kt & 1], kKStride, kpart(st_store));
-    store_rows(v_lds[(kt + 1) & 1], kVStride, vpart(st_store));
+    mx = mx_next;
     __syncthreads();
   };
 
