@@ -276,6 +276,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // scores of tile kt (the previous step) and V tile kt-1's for the previous
   // step's P.V, both before the barrier that ended it.
   auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 *st_store, uint4 *st_load) {
+    // K tile kt+1 and V tile kt are visible since the barrier that ended the
+    // previous step: the first score fragments are read before the ballot,
+    // and the first P.V fragments late in the score phase, so neither read's
+    // latency opens its phase.
+    const uint16_t *kp = kfrag + ((kt + 1) & 1) * (kBc * kKStride);
+    bf16x8 ka[2][2];
+    ka[0][0] = kread(kp, 0, 0);
+    ka[0][1] = kread(kp, 1, 0);
+    const uint16_t *vp = vfrag + (kt & 1) * (kBc * kVStride);
+    bf16x8 vf[2][4];
     // (1)
     if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mx);
@@ -294,17 +304,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     store_rows(v_lds[(kt + 1) & 1], kVStride, vpart(st_store));
     load_kv(Kh, kt + 3, kpart(st_load));
     load_kv(Vh, kt + 2, vpart(st_load));
-    const uint16_t *kp = kfrag + ((kt + 1) & 1) * (kBc * kKStride);
     uint32_t pw[16];
-    bf16x8 ka[2][2];
-    ka[0][0] = kread(kp, 0, 0);
-    ka[0][1] = kread(kp, 1, 0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int cur = c & 1, nxt = cur ^ 1;
       if (c < 7) {
         ka[nxt][0] = kread(kp, 0, c + 1);
         ka[nxt][1] = kread(kp, 1, c + 1);
+      } else {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp + 32 * db);
       }
       s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
@@ -319,7 +328,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run1, false);
       }
       s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][1], qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
-      if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's 2 LDS reads
+      if (c < 7)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's K reads
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // P.V's first V reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
       if (c == 0) __builtin_amdgcn_sched_group_barrier(0x200, kChunks, 0);   // V staging writes
@@ -332,10 +344,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     // + 0..7, the same keys the transposed V reads deliver for k-step
     // bt = 2b + t.  V fragments are read one k-step ahead (ping-pong).
     mask_tile(s_nxt, kt + 1);
-    const uint16_t *vp = vfrag + (kt & 1) * (kBc * kVStride);
-    bf16x8 vf[2][4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp + 32 * db);
     store_rows(k_lds[kt & 1], kKStride, kpart(st_store));
     const float mx_next = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
 #pragma unroll
