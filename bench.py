@@ -234,6 +234,78 @@ def bench_projection(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_split_kv(args):
+    """Attention with the keys cut into P contiguous ranges: P h3_attention_lse
+    launches (one per range, all heads) and one h3_attention_merge, on the
+    ws8 inputs after the prologue.  One JSON line."""
+    import torch
+    from exact_head_attention_amd import binding as B
+    from exact_head_attention_amd import inputs as I
+
+    P = args.parts
+    w = I.WORKLOADS["ws8"]
+    log(f"bench: split-KV attention on {w.name}, {P} key ranges; generating inputs")
+    x = I.make_inputs(w, args.seed)
+    dev = torch.device("cuda:0")
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).view(dt).to(dev)
+
+    q, k, v = (up(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    gq, gk = up(x["gamma_q"], torch.float32), up(x["gamma_k"], torch.float32)
+    cos, sin = B.rope_tables(up(x["positions"], torch.int32), w.D, x["theta"])
+    B.qknorm_rope(q, k, gq, gk, cos, sin, x["eps"])
+    cuts = [round(i * w.L / P / 64) * 64 for i in range(P)] + [w.L]
+    outs = torch.empty((P, w.H, w.L, w.D), dtype=torch.float32, device=dev)
+    lses = torch.empty((P, w.H, w.L), dtype=torch.float32, device=dev)
+    out = torch.empty((w.H, w.L, w.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for p in range(P):
+            B.attention_lse(q, k[:, cuts[p]:cuts[p + 1]], v[:, cuts[p]:cuts[p + 1]], x["scale"], outs[p], lses[p])
+        if ev is not None:
+            ev[1].record(stream)
+        B.attention_merge(outs, lses, out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    total_ms = part_ms + merge_ms
+    flops = w.flops
+    merge_bytes = P * w.H * w.L * (w.D * 4 + 4) + w.H * w.L * w.D * 2
+    rec = {
+        "metric": f"split-KV attention TFLOPS (4*H*L^2*D over {P} key ranges + merge) and % bf16 MFMA peak",
+        "value": round(flops / (total_ms / 1e3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (ws8 inputs after the prologue)",
+        "config": {"workload": f"ws8 attention with the keys cut at {cuts}: {P} h3_attention_lse launches + "
+                               f"one h3_attention_merge", "H": w.H, "L": w.L, "D": w.D, "parts": P},
+        "roofline": {"kernel": "attn_fwd_kernel<true> (all parts)", "bound": "mfma",
+                     "achieved": round(flops / (part_ms / 1e3) / 1e12, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (part_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(part_ms, 4)},
+        "merge": {"kernel": "attn_merge_kernel", "bound": "hbm", "avg_launch_us": round(merge_ms * 1e3, 2),
+                  "achieved_GBps": round(merge_bytes / (merge_ms / 1e3) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
+                  "frac": round(merge_bytes / (merge_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "bytes_per_launch": merge_bytes},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +321,8 @@ def main():
     ap.add_argument("--pmc", nargs="*", default=None)
     ap.add_argument("--command", default="")
     ap.add_argument("--source", default=None, help="kernel source whose hash the summary records")
+    ap.add_argument("--parts", type=int, default=0,
+                    help="time split-KV attention (h3_attention_lse over this many key ranges + merge) on ws8")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
@@ -261,6 +335,9 @@ def main():
         sys.exit(2)
 
     from exact_head_attention_amd import inputs as I
+    if args.parts > 0:
+        bench_split_kv(args)
+        return
     if args.workload in I.PROJ_WORKLOADS:
         bench_projection(args)
         return
