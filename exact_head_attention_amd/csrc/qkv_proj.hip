@@ -53,7 +53,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int D = kHeadDim;          // features per head slot
 constexpr int kSlots = 2;            // head slots (of the 3H q, k, v heads) per workgroup
 constexpr int kTok = 256;            // tokens per workgroup
-constexpr int kThreads = 256;        // 4 waves: (slot, token half)
+#ifndef H3_QKV_THREADS
+#define H3_QKV_THREADS 512
+#endif
+constexpr int kThreads = H3_QKV_THREADS;   // waves (slot, token range): 2 slots x kThreads/128 token ranges
+constexpr int kTS = 1024 / kThreads;       // 32-token sub-tiles per wave
 constexpr int kStepBytes = 64;       // bytes of each row per LDS step
 constexpr int kStride = 40;          // uint16 slots per LDS row (80 B)
 constexpr int kRows = kSlots * D;    // weight rows per workgroup
@@ -91,7 +95,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // scales *x_scale and *w_scale (device scalars).  C counts hidden elements.
 // Head slot j in [0, 3H) is q head j, k head j - H or v head j - 2H.
 template <bool kFp8>
-__global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
+__global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ Wq, const uint8_t *__restrict__ Wk,
     const uint8_t *__restrict__ Wv, const float *__restrict__ x_scale, const float *__restrict__ w_scale,
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
@@ -160,13 +164,13 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
     }
   };
 
-  // Wave (sl, th): head slot sl of the tile, tokens 128 th .. 128 th + 127.
+  // Wave (sl, th): head slot sl of the tile, tokens 32 kTS th .. + 32 kTS - 1.
   const int sl = wave & 1, th = wave >> 1;
-  f32x16 acc[4][4];
+  f32x16 acc[4][kTS];
 #pragma unroll
   for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-    for (int ts = 0; ts < 4; ++ts) acc[fs][ts] = f32x16{};
+    for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] = f32x16{};
 
   const int n_k = row_bytes / kStepBytes;
   load(0);
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
   // 128 th + 32 ts + l32; bf16: bytes 32kk + 16g of the step's 64, fp8: bytes
   // 32g .. 32g+31.
   const uint16_t *wa = &w_lds[0][(sl * D + l32) * kStride + (kFp8 ? 16 : 8) * g];
-  const uint16_t *xb = &x_lds[0][(th * 128 + l32) * kStride + (kFp8 ? 16 : 8) * g];
+  const uint16_t *xb = &x_lds[0][(th * 32 * kTS + l32) * kStride + (kFp8 ? 16 : 8) * g];
   auto frag32 = [](const uint16_t *p) {
     const uint4 lo = *reinterpret_cast<const uint4 *>(p);
     const uint4 hi = *reinterpret_cast<const uint4 *>(p + 8);
@@ -190,31 +194,29 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
     const uint16_t *wab = wa + buf * (kRows * kStride);
     const uint16_t *xbb = xb + buf * (kTok * kStride);
     if constexpr (kFp8) {
-      i32x8 a[4], b[4];
+      i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = frag32(wab + i * 32 * kStride);
-        b[i] = frag32(xbb + i * 32 * kStride);
-      }
+      for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kStride);
+#pragma unroll
+      for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kStride);
 #pragma unroll
       for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts)
+        for (int ts = 0; ts < kTS; ++ts)
           acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
                                                                         kE8M0One, 0, kE8M0One);
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 a[4], b[4];
+        bf16x8 a[4], b[kTS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kStride + 16 * kk);
-          b[i] = *reinterpret_cast<const bf16x8 *>(xbb + i * 32 * kStride + 16 * kk);
-        }
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kStride + 16 * kk);
+#pragma unroll
+        for (int i = 0; i < kTS; ++i) b[i] = *reinterpret_cast<const bf16x8 *>(xbb + i * 32 * kStride + 16 * kk);
 #pragma unroll
         for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-          for (int ts = 0; ts < 4; ++ts)
+          for (int ts = 0; ts < kTS; ++ts)
             acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
       }
     }
@@ -239,11 +241,11 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_kernel(
 #pragma unroll
     for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-      for (int ts = 0; ts < 4; ++ts) acc[fs][ts] *= sc;
+      for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] *= sc;
   }
 #pragma unroll
-  for (int ts = 0; ts < 4; ++ts) {
-    const int t = t0 + th * 128 + ts * 32 + l32;
+  for (int ts = 0; ts < kTS; ++ts) {
+    const int t = t0 + th * 32 * kTS + ts * 32 + l32;
     float r = 1.0f;
     if (which < 2) {
       float ss = 0.f;
