@@ -21,11 +21,11 @@
 //     column and 16 features per lane, so a token's sum of squares over its
 //     128 features is lane-local plus one lane-half exchange, and each RoPE
 //     pair (2j, 2j+1) sits in one lane.
-//   * The hidden dimension streams in steps of 64 bytes per row (32 bf16 or
-//     64 fp8 elements) through double-buffered LDS (80-byte padded rows: 8
-//     consecutive rows hit 8 disjoint bank groups); global loads are buffer
-//     loads one step ahead, so the last partial token tile reads zeros and
-//     writes nothing past L.
+//   * The hidden dimension streams in steps of 128 bytes per row (64 bf16)
+//     or 64 bytes (64 fp8) through double-buffered LDS (rows padded by 16
+//     bytes: 8 consecutive rows hit 8 disjoint bank groups); global loads are
+//     buffer loads one step ahead, so the last partial token tile reads zeros
+//     and writes nothing past L.
 //   * fp8 form: OCP e4m3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
 //     block scales), each lane's fragment 32 consecutive hidden elements of
 //     its row for both operands; any fixed split of a step's elements over
@@ -58,11 +58,7 @@ constexpr int kTok = 256;            // tokens per workgroup
 #endif
 constexpr int kThreads = H3_QKV_THREADS;   // waves (slot, token range): 2 slots x kThreads/128 token ranges
 constexpr int kTS = 1024 / kThreads;       // 32-token sub-tiles per wave
-constexpr int kStepBytes = 64;       // bytes of each row per LDS step
-constexpr int kStride = 40;          // uint16 slots per LDS row (80 B)
 constexpr int kRows = kSlots * D;    // weight rows per workgroup
-constexpr int kWChunks = kRows * (kStepBytes / 16) / kThreads;   // 16-byte chunks per thread per step: 4
-constexpr int kXChunks = kTok * (kStepBytes / 16) / kThreads;    // 4
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
@@ -101,6 +97,13 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
+  // Bytes of each row per LDS step: 128 for bf16 (measured faster), 64 for
+  // fp8 (its 32-byte fragments leave no registers for a longer step).
+  constexpr int kStepBytes = kFp8 ? 64 : 128;
+  constexpr int kCPR = kStepBytes / 16;         // 16-byte pieces per row and step
+  constexpr int kStride = kStepBytes / 2 + 8;   // uint16 slots per LDS row (+16 B: 8 consecutive rows, 8 bank groups)
+  constexpr int kWChunks = kRows * kCPR / kThreads;   // 16-byte staging chunks per thread per step
+  constexpr int kXChunks = kTok * kCPR / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][kRows * kStride];
   __shared__ __attribute__((aligned(16))) uint16_t x_lds[2][kTok * kStride];
 
@@ -132,35 +135,41 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * row_bytes, tok_rows * row_bytes);
 
-  // Staging: chunk c = tid + 256 i of a step covers row c/4 (weight rows
-  // 0..255 over the two slots, or token rows), bytes 16 (c%4) of the step's
-  // 64-byte slice of that row.
+  // Staging: chunk c = tid + kThreads i of a step covers row c / kCPR
+  // (weight rows 0..255 over the two slots, or token rows), piece c % kCPR
+  // of the step's kStepBytes-byte slice of that row.
   uint4 sw[kWChunks], sx[kXChunks];
   auto load = [&](int ks) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
 #pragma unroll
     for (int i = 0; i < kWChunks; ++i) {
-      // Chunks i = 0, 1 are slot 0's rows 0..127, i = 2, 3 slot 1's.
+      // The first half of the chunks are slot 0's rows 0..127, the rest slot 1's.
       constexpr int kPerSlot = kWChunks / kSlots;
-      const int row = (tid >> 2) + (kThreads / 4) * (i % kPerSlot);
-      sw[i] = bload128(rw[i / kPerSlot], row * row_bytes + kb + 16 * (tid & 3));
+      const int row = tid / kCPR + (kThreads / kCPR) * (i % kPerSlot);
+      sw[i] = bload128(rw[i / kPerSlot], row * row_bytes + kb + 16 * (tid % kCPR));
     }
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) {
       const int c = tid + kThreads * i;
-      sx[i] = bload128(rx, (c >> 2) * row_bytes + kb + 16 * (c & 3));
+      sx[i] = bload128(rx, (c / kCPR) * row_bytes + kb + 16 * (c % kCPR));
     }
   };
-  auto store = [&](int buf) {
+  // A row may end half way through its last step (row_bytes is a multiple of
+  // 64): pieces past its end are stored as zeros, so they add nothing.  The
+  // mask is an AND applied here, where the loads have landed anyway.
+  auto store = [&](int buf, int ks) {
+    const uint32_t keep =
+        kStepBytes == 64 || ks * kStepBytes + 16 * (tid % kCPR) < row_bytes ? 0xFFFFFFFFu : 0u;
+    auto masked = [keep](uint4 v) { return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep); };
 #pragma unroll
     for (int i = 0; i < kWChunks; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(&w_lds[buf][(c >> 2) * kStride + 8 * (c & 3)]) = sw[i];
+      *reinterpret_cast<uint4 *>(&w_lds[buf][(c / kCPR) * kStride + 8 * (c % kCPR)]) = masked(sw[i]);
     }
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) {
       const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(&x_lds[buf][(c >> 2) * kStride + 8 * (c & 3)]) = sx[i];
+      *reinterpret_cast<uint4 *>(&x_lds[buf][(c / kCPR) * kStride + 8 * (c % kCPR)]) = masked(sx[i]);
     }
   };
 
@@ -172,9 +181,9 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
 #pragma unroll
     for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] = f32x16{};
 
-  const int n_k = row_bytes / kStepBytes;
+  const int n_k = (row_bytes + kStepBytes - 1) / kStepBytes;
   load(0);
-  store(0);
+  store(0, 0);
   if (n_k > 1) load(1);
   __syncthreads();
 
@@ -194,20 +203,23 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
     const uint16_t *wab = wa + buf * (kRows * kStride);
     const uint16_t *xbb = xb + buf * (kTok * kStride);
     if constexpr (kFp8) {
-      i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kStride);
+      for (int kk = 0; kk < kStepBytes / 64; ++kk) {
+        i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kStride);
+        for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kStride + 32 * kk);
 #pragma unroll
-      for (int fs = 0; fs < 4; ++fs)
+        for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kStride + 32 * kk);
 #pragma unroll
-        for (int ts = 0; ts < kTS; ++ts)
-          acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
-                                                                        kE8M0One, 0, kE8M0One);
+        for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+          for (int ts = 0; ts < kTS; ++ts)
+            acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
+                                                                          kE8M0One, 0, kE8M0One);
+      }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < kStepBytes / 32; ++kk) {
         bf16x8 a[4], b[kTS];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kStride + 16 * kk);
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
     if (ks + 1 < n_k) {
       // Buffer buf^1 was last read in step ks-1, before the barrier that
       // ended it; step ks+2's loads refill the staging registers.
-      store(buf ^ 1);
+      store(buf ^ 1, ks + 1);
       if (ks + 2 < n_k) load(ks + 2);
     }
     __syncthreads();
