@@ -4,9 +4,15 @@
 // 256 B) is read once and written once, in place.  One 16-lane row of a wave
 // owns one token: each lane holds 8 consecutive elements (one 16-byte load),
 // i.e. four adjacent RoPE pairs, so the pair rotation is lane-local and only
-// the sum of squares crosses lanes (a 16-lane DPP reduction).  The token's cos
-// and sin (64 fp32 each, shared by every head) are loaded once and reused for
-// all H heads of q and of k, so the tables cross HBM once per token.
+// the sum of squares crosses lanes (a 16-lane DPP reduction).
+//
+// A workgroup is 16 tokens of one head, and workgroups are numbered head by
+// head, so the whole chip streams through one head's q and k at a time: two
+// long sequential streams, which DRAM serves better (45.5 us cold at H = 7,
+// L = 32768, 5.5 TB/s) than every workgroup walking all H heads at once
+// (50.4 us).  The cos/sin rows are re-read for every head; after the first
+// head they come from cache, so HBM still sees the tables about once.
+// Non-temporal loads and stores measured best (plain ones: 52-53 us).
 //
 // Math follows "Tensor parallelism for MiniMax-H3", PR description (head_dim-
 // shaped QK-norm after the head split; real cos/sin broadcast over heads):
@@ -21,16 +27,26 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef H3_PRO_LNT
+#define H3_PRO_LNT 1
+#endif
+#ifndef H3_PRO_SNT
+#define H3_PRO_SNT 1
+#endif
 // q and k rows are touched exactly once: stream them past the caches.
 __device__ __forceinline__ uint4 load_stream(const uint16_t *p) {
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+  if (H3_PRO_LNT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+  return *reinterpret_cast<const uint4 *>(p);
 }
 __device__ __forceinline__ void store_stream(uint16_t *p, uint4 v) {
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+  if (H3_PRO_SNT) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+  else *reinterpret_cast<uint4 *>(p) = v;
 }
 
-constexpr int kTokensPerBlock = 16;   // 256 threads = 16 rows of 16 lanes
-constexpr int kHeadUnroll = 4;        // heads whose loads are in flight together
+#ifndef H3_PRO_TPB
+#define H3_PRO_TPB 16
+#endif
+constexpr int kTokensPerBlock = H3_PRO_TPB;   // 16 lanes per token
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -75,14 +91,19 @@ __device__ __forceinline__ uint4 norm_rope8(uint4 raw, const float g[8], const f
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ __launch_bounds__(256) void qknorm_rope_kernel(
+__global__ __launch_bounds__(kTokensPerBlock * 16) void qknorm_rope_kernel(
     uint16_t *__restrict__ q, uint16_t *__restrict__ k, const float *__restrict__ gamma_q,
     const float *__restrict__ gamma_k, const float *__restrict__ cos_t,
-    const float *__restrict__ sin_t, int H, int L, float eps) {
+    const float *__restrict__ sin_t, int L, int n_tblocks, float eps) {
+  const int head = blockIdx.x / n_tblocks;
+  const int tb = blockIdx.x - head * n_tblocks;
   const int sub = threadIdx.x & 15;                       // lane within the 16-lane row
-  const int tok = blockIdx.x * kTokensPerBlock + (threadIdx.x >> 4);
+  const int tok = tb * kTokensPerBlock + (threadIdx.x >> 4);
   if (tok >= L) return;                                   // whole 16-lane rows exit together
 
+  const size_t off = (static_cast<size_t>(head) * L + tok) * kHeadDim + 8 * sub;
+  const uint4 rq = load_stream(q + off);
+  const uint4 rk = load_stream(k + off);
   const float4 c4 = *reinterpret_cast<const float4 *>(cos_t + static_cast<size_t>(tok) * 64 + 4 * sub);
   const float4 s4 = *reinterpret_cast<const float4 *>(sin_t + static_cast<size_t>(tok) * 64 + 4 * sub);
   const float c[4] = {c4.x, c4.y, c4.z, c4.w};
@@ -96,26 +117,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     gq[0] = a.x; gq[1] = a.y; gq[2] = a.z; gq[3] = a.w; gq[4] = b.x; gq[5] = b.y; gq[6] = b.z; gq[7] = b.w;
     gk[0] = e.x; gk[1] = e.y; gk[2] = e.z; gk[3] = e.w; gk[4] = f.x; gk[5] = f.y; gk[6] = f.z; gk[7] = f.w;
   }
-
-  const size_t head_stride = static_cast<size_t>(L) * kHeadDim;
-  const size_t row_off = static_cast<size_t>(tok) * kHeadDim + 8 * sub;
-  for (int h0 = 0; h0 < H; h0 += kHeadUnroll) {
-    uint4 rq[kHeadUnroll], rk[kHeadUnroll];
-#pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u) {
-      if (h0 + u < H) {
-        rq[u] = load_stream(q + (h0 + u) * head_stride + row_off);
-        rk[u] = load_stream(k + (h0 + u) * head_stride + row_off);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kHeadUnroll; ++u) {
-      if (h0 + u < H) {
-        store_stream(q + (h0 + u) * head_stride + row_off, norm_rope8(rq[u], gq, c, s, eps));
-        store_stream(k + (h0 + u) * head_stride + row_off, norm_rope8(rk[u], gk, c, s, eps));
-      }
-    }
-  }
+  store_stream(q + off, norm_rope8(rq, gq, c, s, eps));
+  store_stream(k + off, norm_rope8(rk, gk, c, s, eps));
 }
 
 // cos/sin of positions[i] * theta^(-2j/D) in fp64, rounded once to fp32.
@@ -139,9 +142,10 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(const int *__restrict_
 hipError_t launch_qknorm_rope(uint16_t *q, uint16_t *k, const float *gamma_q, const float *gamma_k,
                               const float *cos_t, const float *sin_t, int H, int L, float eps,
                               hipStream_t stream) {
-  const int blocks = (L + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(blocks), dim3(256), 0, stream, q, k, gamma_q, gamma_k,
-                     cos_t, sin_t, H, L, eps);
+  const int n_tblocks = (L + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int64_t blocks = static_cast<int64_t>(H) * n_tblocks;   // < 2^31: H*L < 2^31 is validated
+  hipLaunchKernelGGL(qknorm_rope_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kTokensPerBlock * 16), 0, stream,
+                     q, k, gamma_q, gamma_k, cos_t, sin_t, L, n_tblocks, eps);
   return hipGetLastError();
 }
 
