@@ -9,8 +9,12 @@
 //   * Work unit = one (head, 256-query tile); each wave owns 32 query rows.
 //     A unit runs as one 8-wave workgroup, or, in the tail launch, as two
 //     4-wave workgroups of 128 rows each (see launch_split below).
-//   * Keys stream in tiles of 64 through double-buffered LDS: K row-major
-//     [key][d], V transposed [d][key] (the transpose happens on the way in).
+//   * Keys stream in tiles of 64 through a 4-slot LDS ring per tensor, K and
+//     V both row-major [key][d] with an XOR swizzle of the 16-byte chunks.
+//     Tiles move from global memory straight into LDS (buffer loads with the
+//     LDS-destination bit), three tiles ahead of the one being multiplied,
+//     so no registers stage them and a load has two steps to land.  V is
+//     read as the transposed MFMA operand with ds_read_b64_tr_b16.
 //   * Per wave and key tile, with v_mfma_f32_32x32x16_bf16:
 //       S^T (64 keys x 32 queries) = K_tile . Q^T        16 MFMAs, Q^T in VGPRs
 //       O^T (128 d  x 32 queries) += V_tile^T . P^T      16 MFMAs
@@ -27,12 +31,14 @@
 //
 // Determinism: a row's arithmetic depends only on its (head, row) and keys
 // are visited in a fixed order; 8- and 4-wave workgroups run the same per-wave
-// code and differ only in how many LDS staging chunks each thread carries.  So
-// every head's output is bit-identical however many heads one launch covers.
+// code and differ only in how many tile loads each wave issues.  So every
+// head's output is bit-identical however many heads one launch covers.
 // The XCD-aware block remap and the main/tail split change only where and
 // when a row runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "h3attn_internal.h"
 
@@ -49,8 +55,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = kHeadDim;
 constexpr int kUnitRows = 256;       // query rows per work unit (8 waves x 32)
 constexpr int kBc = 64;              // keys per tile
-constexpr int kKStride = D + 8;      // bf16 per K row in LDS (272 B: rows shift 4 banks)
-constexpr int kVStride = D + 32;     // bf16 per V row in LDS (320 B: transpose reads hit 4 disjoint bank windows)
+constexpr int kSlots = 4;            // LDS ring depth (tiles) for each of K and V
+constexpr int kTileElems = kBc * D;  // one tile, rows of 256 B without padding
 constexpr float kLog2e = 1.4426950408889634f;
 // The running max is raised only when some row of the wave sees a larger
 // score (a wave-uniform branch, taken a few dozen times per 32-row block over
@@ -71,6 +77,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Buffer loads: the hardware returns zeros past num_records bytes, so ragged
 // tails need no branches and never touch memory outside the head.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)(p)));
+}
+
+// 16-byte chunk swizzles inside a 256-byte LDS row (chunk index ^ swizzle).
+//   K: row & 15 -- a fragment read takes one logical chunk from 16 rows that
+//      differ in their low four bits, which then sit in 16 distinct chunks.
+//   V: 4 (row & 3) -- a transposed read takes 4 chunks (bits 0-1) from 4
+//      consecutive rows, which then sit in 4 disjoint groups of 4 chunks.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
 }
@@ -125,10 +144,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
   constexpr int kThreads = NW * 64;
   constexpr int kParts = 8 / NW;           // workgroups per unit
-  constexpr int kChunks = 16 / NW;         // 16-byte staging chunks per thread per tensor and tile
+  constexpr int kDma = 16 / NW;            // 1 KB DMA instructions per wave per tensor and tile
   static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBc * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBc * kVStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kSlots][kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -159,41 +178,42 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, (wave * 32 + l32) * row_bytes + 32 * c + 16 * g));
   }
 
-  // Staging of one key tile: 64 rows x 16 chunks of 16 B for each of K and
-  // V; thread takes chunks tid + i * kThreads, i < kChunks (tile-relative
-  // byte offset chunk * 16).  Both land row-major in LDS.
-  using Chunks = uint4[kChunks];
-  auto load_kv = [&](const uint16_t *base, int kt, Chunks &r) {
-    const int keys_left = Lk - kt * kBc;
+  // Tiles go from global memory straight into LDS (buffer loads with the
+  // LDS-destination bit).  Instruction j of wave w writes rows
+  // 4n .. 4n+3, n = w + NW j, as one contiguous kilobyte: lane i lands in
+  // row 4n + i/16 at physical chunk i%16, so it fetches the row's logical
+  // chunk (i%16) ^ swizzle.  Keys at or past Lk read as zeros (the
+  // descriptor covers only the tile's valid rows).  The loads are tracked by
+  // the vector-memory counter only; the waits below are explicit.
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
+    const int keys_left = Lk - t * kBc;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(base + static_cast<size_t>(kt) * kBc * D, (keys_left < kBc ? keys_left : kBc) * row_bytes);
+        make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) r[i] = bload128(rs, (tid + kThreads * i) * 16);
-  };
-  auto store_rows = [&](uint16_t *dst, int stride, const Chunks &r) {
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(dst + (c >> 4) * stride + (c & 15) * 8) = r[i];
+    for (int j = 0; j < kDma; ++j) {
+      const int n = wave + NW * j;
+      const int row = 4 * n + (lane >> 4);
+      const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
+      const uint32_t m0 = lds_addr(dst) + (wave_u + NW * j) * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0), "v"(row * row_bytes + 16 * chunk), "s"(rs)
+                   : "memory");
     }
   };
+  // Tiles are loaded V first, then K (2 kDma instructions per wave).  Waiting
+  // until at most one tile's loads are outstanding completes all older ones.
+  auto dma_pair = [&](int t) {
+    dma_tile(Vh, t, v_lds[t % kSlots], false);
+    dma_tile(Kh, t, k_lds[t % kSlots], true);
+  };
+  auto dma_wait_all_but_one_pair = [&]() {
+    if constexpr (kDma == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  };
 
-  // S^T = K_tile . Q^T for the tile in k_lds[buf]; two independent chains.
   const int krow = swap_bits23(l32);
-  auto compute_s = [&](int buf, f32x16 (&s)[2]) {
-    const uint16_t *kp0 = &k_lds[buf][krow * kKStride + 8 * g];
-    const uint16_t *kp1 = kp0 + 32 * kKStride;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kp0 + 16 * c);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kp1 + 16 * c);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[1], 0, 0, 0);
-    }
-  };
-
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
@@ -201,38 +221,43 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   float l_run0 = 0.f, l_run1 = 0.f; // this lane's partial row sums of the bf16 weights
 
   const int n_kt = (Lk + kBc - 1) / kBc;
-  // Staging registers, two sets: a step stores the set loaded one step
-  // earlier and refills the other, so global-load latency hides behind a
-  // whole step.  Set layout: [0, kChunks) K chunks, [kChunks, 2 kChunks) V.
-  uint4 stage0[2 * kChunks], stage1[2 * kChunks];
-  auto kpart = [](uint4 *st) -> Chunks & { return *reinterpret_cast<Chunks *>(st); };
-  auto vpart = [](uint4 *st) -> Chunks & { return *reinterpret_cast<Chunks *>(st + kChunks); };
-  {
-    uint4 k0[kChunks], v0[kChunks], k1[kChunks];
-    load_kv(Kh, 0, k0);
-    load_kv(Vh, 0, v0);
-    load_kv(Kh, 1, k1);
-    load_kv(Kh, 2, kpart(stage0));
-    load_kv(Vh, 1, vpart(stage0));
-    store_rows(k_lds[0], kKStride, k0);
-    store_rows(v_lds[0], kVStride, v0);
-    store_rows(k_lds[1], kKStride, k1);
-  }
+  // Steps run in groups of kSlots so that every ring slot is a compile-time
+  // constant; the up to kSlots-1 extra tiles lie wholly past Lk, so their
+  // weights are exactly 0 and their (zero-filled) V rows add exact zeros.
+  const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;
+  dma_pair(0);
+  dma_pair(1);
+  dma_pair(2);
+  dma_wait_all_but_one_pair();   // tiles 0 and 1 are in LDS (this wave's share)
   __syncthreads();
 
-  const uint16_t *kfrag = &k_lds[0][swap_bits23(l32) * kKStride + 8 * g];
+  // K fragment of chunk pair c: row krow (+32 for the second key block),
+  // logical chunk 2c + g, i.e. physical chunk 2c ^ (g ^ (krow & 15)).
+  int koff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) koff[c] = krow * D + 8 * ((2 * c) ^ (g ^ k_swz(krow)));
   // Transposed V reads: within each 16-lane group, lane L names row
   // 8g + L/4 (+4 for the second read) and columns 16*dhalf + 4*(L%4) .. +3;
   // the hardware hands lane j of the group column 16*dhalf + j of the four
   // named rows, i.e. V[8g + 0..7][32db + l32] across the two reads.
-  const uint16_t *vfrag = &v_lds[0][(8 * g + ((lane & 15) >> 2)) * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)];
-  auto vread = [&](const uint16_t *src) {
+  // The columns of d block db sit in logical chunk 4db + 2 dhalf + (L%4)/2 of
+  // rows 8g + L/4 (+16 per k-step, +4 for the second read), whose swizzle
+  // 4 (row & 3) depends on L only.
+  int voff[4];
+  {
+    const int vrow = 8 * g + ((lane & 15) >> 2);
+    const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) voff[db] = vrow * D + 8 * ((4 * db + vch) ^ v_swz(vrow)) + 4 * (lane & 1);
+  }
+  auto vread = [&](const uint16_t *vt, int bt, int db) {
+    const uint16_t *src = vt + voff[db] + 16 * bt * D;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * kVStride));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto kread = [&](const uint16_t *kp, int b, int c) {
-    return *reinterpret_cast<const bf16x8 *>(kp + b * 32 * kKStride + 16 * c);
+  auto kread = [&](const uint16_t *kt_lds, int b, int c) {
+    return *reinterpret_cast<const bf16x8 *>(kt_lds + koff[c] + b * 32 * D);
   };
 
   // Mask the keys of tile t at or past Lk (only the last, ragged tile has any).
@@ -254,8 +279,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     s_a[1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kfrag, 0, c), qf[c], s_a[0], 0, 0, 0);
-      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kfrag, 1, c), qf[c], s_a[1], 0, 0, 0);
+      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], 0, c), qf[c], s_a[0], 0, 0, 0);
+      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], 1, c), qf[c], s_a[1], 0, 0, 0);
     }
   }
   mask_tile(s_a, 0);
@@ -267,24 +292,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // their shadow, so the two waves sharing a SIMD (kept in step by the
   // barrier) leave the matrix pipe idle only around that barrier:
   //   (1) raise the running max if tile kt's max (found last step) exceeds it;
-  //   (2) scores of tile kt+1 on the matrix cores, interleaved with tile kt's
-  //       exponentials, with V tile kt+1 staged to LDS and the global loads
-  //       of K tile kt+3 and V tile kt+2 issued in between;
-  //   (3) O += P.V for tile kt, interleaved with tile kt+1's row max and the
-  //       LDS staging of K tile kt+2.
-  // The staged buffers are free: K tile kt's buffer was last read for the
-  // scores of tile kt (the previous step) and V tile kt-1's for the previous
-  // step's P.V, both before the barrier that ended it.
-  auto step = [&](int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint4 *st_store, uint4 *st_load) {
+  //   (2) the loads of tile kt+3 into ring slot (kt+3) % kSlots, then the
+  //       scores of tile kt+1 on the matrix cores, interleaved with tile kt's
+  //       exponentials;
+  //   (3) O += P.V for tile kt, interleaved with tile kt+1's row max;
+  //   (4) wait for this wave's loads of tile kt+2, then the barrier.
+  // Slot (kt+3) % kSlots last held tile kt-1, whose K was read for the
+  // scores of step kt-2 and whose V for the P.V of step kt-1, both before
+  // the barrier that ended step kt-1.  R = kt % kSlots, a compile-time value.
+  auto step = [&](auto r_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int R = decltype(r_c)::value;
     // K tile kt+1 and V tile kt are visible since the barrier that ended the
     // previous step: the first score fragments are read before the ballot,
     // and the first P.V fragments late in the score phase, so neither read's
     // latency opens its phase.
-    const uint16_t *kp = kfrag + ((kt + 1) & 1) * (kBc * kKStride);
+    const uint16_t *kp = k_lds[(R + 1) % kSlots];
     bf16x8 ka[2][2];
     ka[0][0] = kread(kp, 0, 0);
     ka[0][1] = kread(kp, 1, 0);
-    const uint16_t *vp = vfrag + (kt & 1) * (kBc * kVStride);
+    const uint16_t *vp = v_lds[R];
     bf16x8 vf[2][4];
     // (1)
     if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
@@ -301,9 +327,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const float neg_m = -m_run;
 
     // (2) K fragments are read one MFMA pair ahead (ping-pong registers).
-    store_rows(v_lds[(kt + 1) & 1], kVStride, vpart(st_store));
-    load_kv(Kh, kt + 3, kpart(st_load));
-    load_kv(Vh, kt + 2, vpart(st_load));
+    dma_tile(Vh, kt + 3, v_lds[(R + 3) % kSlots], false);
+    dma_tile(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
     uint32_t pw[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -313,7 +338,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         ka[nxt][1] = kread(kp, 1, c + 1);
       } else {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp + 32 * db);
+        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, 0, db);
       }
       s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
@@ -334,8 +359,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // P.V's first V reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
-      if (c == 0) __builtin_amdgcn_sched_group_barrier(0x200, kChunks, 0);   // V staging writes
-      if (c == 1 || c == 2) __builtin_amdgcn_sched_group_barrier(0x020, kChunks, 0);   // global loads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
     }
@@ -344,21 +367,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     // + 0..7, the same keys the transposed V reads deliver for k-step
     // bt = 2b + t.  V fragments are read one k-step ahead (ping-pong).
     mask_tile(s_nxt, kt + 1);
-    store_rows(k_lds[kt & 1], kKStride, kpart(st_store));
     const float mx_next = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
       const int cur = bt & 1, nxt = cur ^ 1;
       if (bt < 3) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp + (16 * (bt + 1)) * kVStride + 32 * db);
+        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, bt + 1, db);
       }
       const uint4 w = make_uint4(pw[4 * bt], pw[4 * bt + 1], pw[4 * bt + 2], pw[4 * bt + 3]);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], __builtin_bit_cast(bf16x8, w), o[db], 0, 0, 0);
       if (bt < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next k-step's V reads
-      if (bt == 0) __builtin_amdgcn_sched_group_barrier(0x200, kChunks, 0);   // K staging writes
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
@@ -366,15 +387,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       }
     }
     mx = mx_next;
+    // (4)
+    dma_wait_all_but_one_pair();
     __syncthreads();
   };
 
-  int kt = 0;
-  for (; kt + 1 < n_kt; kt += 2) {
-    step(kt, s_a, s_b, stage0, stage1);
-    step(kt + 1, s_b, s_a, stage1, stage0);
+  for (int kt = 0; kt < n_steps; kt += kSlots) {
+    step(std::integral_constant<int, 0>{}, kt, s_a, s_b);
+    step(std::integral_constant<int, 1>{}, kt + 1, s_b, s_a);
+    step(std::integral_constant<int, 2>{}, kt + 2, s_a, s_b);
+    step(std::integral_constant<int, 3>{}, kt + 3, s_b, s_a);
   }
-  if (kt < n_kt) step(kt, s_a, s_b, stage0, stage1);
+  // Loads of tiles past the end are still in flight: they must land before
+  // the workgroup's LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const float l_run = l_run0 + l_run1;
 
   // Epilogue: full row sum, normalise, round once to bf16 (or keep fp32 and
