@@ -11,9 +11,9 @@
 //
 // Work decomposition
 //   * Workgroup = (feature tile, token tile): two head slots (256 output
-//     features; slot j of the 3H q, k, v heads) x 256 tokens; 4 waves, each
-//     one head slot (128 features) x 128 tokens, with its 16 accumulator
-//     tiles (256 registers) in AGPRs: one wave per SIMD.
+//     features; slot j of the 3H q, k, v heads) x 256 tokens; 8 waves, each
+//     one head slot (128 features) x 64 tokens with its 8 accumulator tiles
+//     (128 registers): two waves per SIMD.
 //   * The product is computed transposed, C^T = W . X^T, with
 //     v_mfma_f32_32x32x16_bf16: A = weight rows (features), B = hidden rows
 //     (tokens).  Both operands are K-contiguous in memory, so every fragment
@@ -21,11 +21,14 @@
 //     column and 16 features per lane, so a token's sum of squares over its
 //     128 features is lane-local plus one lane-half exchange, and each RoPE
 //     pair (2j, 2j+1) sits in one lane.
-//   * The hidden dimension streams in steps of 128 bytes per row (64 bf16)
-//     or 64 bytes (64 fp8) through double-buffered LDS (rows padded by 16
-//     bytes: 8 consecutive rows hit 8 disjoint bank groups); global loads are
-//     buffer loads one step ahead, so the last partial token tile reads zeros
-//     and writes nothing past L.
+//   * The hidden dimension streams in steps of 64 bytes per row (32 bf16 or
+//     64 fp8 elements) through a 4-slot LDS ring: buffer loads with the
+//     LDS-destination bit put each step's 256 weight rows and 256 token rows
+//     in LDS three steps ahead, with no register staging.  Rows are 64 bytes
+//     with their four 16-byte chunks swizzled by (row / 4) % 4, so the 16
+//     rows of a fragment read hit 16 distinct bank groups.  The descriptor
+//     ranges make the last partial token tile (and an odd 3H's empty head
+//     slot) read zeros, and nothing is written past L.
 //   * fp8 form: OCP e4m3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
 //     block scales), each lane's fragment 32 consecutive hidden elements of
 //     its row for both operands; any fixed split of a step's elements over
@@ -38,6 +41,8 @@
 //     L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "h3attn_internal.h"
 
@@ -61,6 +66,11 @@ constexpr int kTS = 1024 / kThreads;       // 32-token sub-tiles per wave
 constexpr int kRows = kSlots * D;    // weight rows per workgroup
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
+constexpr int kStepBytes = 64;       // bytes of each row per step (32 bf16 or 64 fp8 hidden elements)
+constexpr int kRowElems = kStepBytes / 2;   // uint16 per LDS row (no padding)
+constexpr int kRing = 4;             // LDS ring depth (steps) for each of W and X
+constexpr int kWaves = kThreads / 64;
+constexpr int kDmaPerStep = 2 * 16 / kWaves;   // 1 KB loads per wave per step (W and X, 16 KB each)
 constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -69,6 +79,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 __device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)(p)));
+}
+
+// Chunk swizzle inside a 64-byte LDS row (4 chunks of 16 bytes): a fragment
+// read takes one logical chunk from 16 consecutive rows; rows 4 apart share
+// banks, and the swizzle puts those 4 rows in 4 different chunks.
+__device__ __forceinline__ int row_swz(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
@@ -97,15 +117,8 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
-  // Bytes of each row per LDS step: 128 for bf16 (measured faster), 64 for
-  // fp8 (its 32-byte fragments leave no registers for a longer step).
-  constexpr int kStepBytes = kFp8 ? 64 : 128;
-  constexpr int kCPR = kStepBytes / 16;         // 16-byte pieces per row and step
-  constexpr int kStride = kStepBytes / 2 + 8;   // uint16 slots per LDS row (+16 B: 8 consecutive rows, 8 bank groups)
-  constexpr int kWChunks = kRows * kCPR / kThreads;   // 16-byte staging chunks per thread per step
-  constexpr int kXChunks = kTok * kCPR / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][kRows * kStride];
-  __shared__ __attribute__((aligned(16))) uint16_t x_lds[2][kTok * kStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t w_lds[kRing][kRows * kRowElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t x_lds[kRing][kTok * kRowElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -135,41 +148,47 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * row_bytes, tok_rows * row_bytes);
 
-  // Staging: chunk c = tid + kThreads i of a step covers row c / kCPR
-  // (weight rows 0..255 over the two slots, or token rows), piece c % kCPR
-  // of the step's kStepBytes-byte slice of that row.
-  uint4 sw[kWChunks], sx[kXChunks];
-  auto load = [&](int ks) {
+  // Steps go from global memory straight into LDS (buffer loads with the
+  // LDS-destination bit), three steps ahead of the one being multiplied.
+  // Load j of wave w writes rows 16n .. 16n+15 (n = w + kWaves j) of the
+  // step's 256 weight rows or 256 token rows as one contiguous kilobyte: lane
+  // i lands in row 16n + i/4 at physical chunk i%4 and fetches the row's
+  // logical chunk (i%4) ^ swizzle.  Rows past 3H or past L read as zeros
+  // (descriptor range).  The waits below are explicit.
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dma_row = lane >> 2;
+  auto dma_step = [&](int ks, int slot) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
 #pragma unroll
-    for (int i = 0; i < kWChunks; ++i) {
-      // The first half of the chunks are slot 0's rows 0..127, the rest slot 1's.
-      constexpr int kPerSlot = kWChunks / kSlots;
-      const int row = tid / kCPR + (kThreads / kCPR) * (i % kPerSlot);
-      sw[i] = bload128(rw[i / kPerSlot], row * row_bytes + kb + 16 * (tid % kCPR));
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int n = wave + kWaves * j;          // weight rows 16n.., head slot n / 8
+      const int row = 16 * n + dma_row;
+      const int ch = (lane & 3) ^ row_swz(row);
+      const uint32_t m0 = lds_addr(w_lds[slot]) + (wave_u + kWaves * j) * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0), "v"((row & (D - 1)) * row_bytes + kb + 16 * ch), "s"(rw[(kWaves * j) / 8])
+                   : "memory");
     }
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
-      const int c = tid + kThreads * i;
-      sx[i] = bload128(rx, (c / kCPR) * row_bytes + kb + 16 * (c % kCPR));
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int row = 16 * (wave + kWaves * j) + dma_row;
+      const int ch = (lane & 3) ^ row_swz(row);
+      const uint32_t m0 = lds_addr(x_lds[slot]) + (wave_u + kWaves * j) * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rx)
+                   : "memory");
     }
   };
-  // A row may end half way through its last step (row_bytes is a multiple of
-  // 64): pieces past its end are stored as zeros, so they add nothing.  The
-  // mask is an AND applied here, where the loads have landed anyway.
-  auto store = [&](int buf, int ks) {
-    const uint32_t keep =
-        kStepBytes == 64 || ks * kStepBytes + 16 * (tid % kCPR) < row_bytes ? 0xFFFFFFFFu : 0u;
-    auto masked = [keep](uint4 v) { return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep); };
-#pragma unroll
-    for (int i = 0; i < kWChunks; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(&w_lds[buf][(c / kCPR) * kStride + 8 * (c % kCPR)]) = masked(sw[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4 *>(&x_lds[buf][(c / kCPR) * kStride + 8 * (c % kCPR)]) = masked(sx[i]);
+  // Wait until this wave's loads of every step but the last `ahead` issued
+  // have landed.
+  auto dma_wait = [&](int ahead) {
+    if (ahead >= 2) {
+      if constexpr (kDmaPerStep == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
 
@@ -181,50 +200,56 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
 #pragma unroll
     for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] = f32x16{};
 
-  const int n_k = (row_bytes + kStepBytes - 1) / kStepBytes;
-  load(0);
-  store(0, 0);
-  if (n_k > 1) load(1);
+  const int n_k = row_bytes / kStepBytes;   // hidden is a multiple of the step (the API checks)
+#pragma unroll
+  for (int r = 0; r < kRing - 1; ++r)
+    if (r < n_k) dma_step(r, r);
+  dma_wait(n_k > 2 ? 2 : 0);   // step 0 is in LDS (this wave's share)
   __syncthreads();
 
   // Fragment addresses: A = weight row 128 sl + 32 fs + l32, B = token row
-  // 128 th + 32 ts + l32; bf16: bytes 32kk + 16g of the step's 64, fp8: bytes
-  // 32g .. 32g+31.
-  const uint16_t *wa = &w_lds[0][(sl * D + l32) * kStride + (kFp8 ? 16 : 8) * g];
-  const uint16_t *xb = &x_lds[0][(th * 32 * kTS + l32) * kStride + (kFp8 ? 16 : 8) * g];
-  auto frag32 = [](const uint16_t *p) {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(p);
-    const uint4 hi = *reinterpret_cast<const uint4 *>(p + 8);
+  // 32 kTS th + 32 ts + l32, both with swizzle (l32 >> 2) & 3.  bf16: logical
+  // chunk 2kk + g; fp8: logical chunks 2g and 2g+1 (32 bytes).
+  const int sw_l = row_swz(l32);
+  const uint16_t *wa = &w_lds[0][(sl * D + l32) * kRowElems];
+  const uint16_t *xb = &x_lds[0][(th * 32 * kTS + l32) * kRowElems];
+  const int c0 = 8 * ((kFp8 ? 2 * g : g) ^ sw_l);   // uint16 offset of the first chunk
+  const int c1 = 8 * ((kFp8 ? 2 * g + 1 : 2 + g) ^ sw_l);
+  auto frag32 = [](const uint16_t *p0, const uint16_t *p1) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(p0);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(p1);
     return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
                  static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
   };
-  for (int ks = 0; ks < n_k; ++ks) {
-    const int buf = ks & 1;
-    const uint16_t *wab = wa + buf * (kRows * kStride);
-    const uint16_t *xbb = xb + buf * (kTok * kStride);
+  // Step ks multiplies slot ks % kRing (R, a compile-time value) after
+  // issuing step ks+3 into slot (ks+3) % kRing, which held step ks-1: every
+  // wave finished reading it before the barrier that ended step ks-1.
+  auto step = [&](auto r_c, int ks) {
+    constexpr int R = decltype(r_c)::value;
+    if (ks + kRing - 1 < n_k) dma_step(ks + kRing - 1, (R + kRing - 1) % kRing);
+    const uint16_t *wab = wa + R * (kRows * kRowElems);
+    const uint16_t *xbb = xb + R * (kTok * kRowElems);
     if constexpr (kFp8) {
+      i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int kk = 0; kk < kStepBytes / 64; ++kk) {
-        i32x8 a[4], b[kTS];
+      for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kRowElems + c0, wab + i * 32 * kRowElems + c1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kStride + 32 * kk);
+      for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kRowElems + c0, xbb + i * 32 * kRowElems + c1);
 #pragma unroll
-        for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kStride + 32 * kk);
+      for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
-        for (int fs = 0; fs < 4; ++fs)
-#pragma unroll
-          for (int ts = 0; ts < kTS; ++ts)
-            acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
-                                                                          kE8M0One, 0, kE8M0One);
-      }
+        for (int ts = 0; ts < kTS; ++ts)
+          acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
+                                                                        kE8M0One, 0, kE8M0One);
     } else {
 #pragma unroll
-      for (int kk = 0; kk < kStepBytes / 32; ++kk) {
+      for (int kk = 0; kk < 2; ++kk) {
+        const int cc = kk == 0 ? c0 : c1;
         bf16x8 a[4], b[kTS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kStride + 16 * kk);
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kRowElems + cc);
 #pragma unroll
-        for (int i = 0; i < kTS; ++i) b[i] = *reinterpret_cast<const bf16x8 *>(xbb + i * 32 * kStride + 16 * kk);
+        for (int i = 0; i < kTS; ++i) b[i] = *reinterpret_cast<const bf16x8 *>(xbb + i * 32 * kRowElems + cc);
 #pragma unroll
         for (int fs = 0; fs < 4; ++fs)
 #pragma unroll
@@ -232,13 +257,15 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
             acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
       }
     }
-    if (ks + 1 < n_k) {
-      // Buffer buf^1 was last read in step ks-1, before the barrier that
-      // ended it; step ks+2's loads refill the staging registers.
-      store(buf ^ 1, ks + 1);
-      if (ks + 2 < n_k) load(ks + 2);
-    }
+    // Step ks+1 must be in LDS: it was issued two steps before the newest.
+    dma_wait(n_k - 1 - ks > 2 ? 2 : 0);
     __syncthreads();
+  };
+  for (int ks = 0; ks < n_k; ks += kRing) {
+    step(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < n_k) step(std::integral_constant<int, 1>{}, ks + 1);
+    if (ks + 2 < n_k) step(std::integral_constant<int, 2>{}, ks + 2);
+    if (ks + 3 < n_k) step(std::integral_constant<int, 3>{}, ks + 3);
   }
 
   // Epilogue.  acc[fs][ts][i] = feature 32fs + 8(i/4) + 4g + i%4 of the
