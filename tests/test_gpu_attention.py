@@ -44,7 +44,9 @@ def _raw(H, L, seed, mult=1.0):
             for _ in range(3)]
 
 
-@pytest.mark.parametrize("L", [1, 2, 7, 63, 64, 65, 127, 255, 256, 257, 513, 1000])
+# Key-tile counts 1..16 cover every position of the last tile in the 4-step
+# loop (129, 192: 3 tiles; 385: 7; 700: 11), as well as ragged and whole tiles.
+@pytest.mark.parametrize("L", [1, 2, 7, 63, 64, 65, 127, 129, 192, 255, 256, 257, 385, 513, 700, 1000])
 def test_attention_ragged_lengths_all_rows(gpu_lib, L):
     q, k, v = _raw(2, L, seed=100 + L)
     _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), label=f"L={L}")
