@@ -34,6 +34,8 @@ HBM_PEAK_GBS = 8000.0               # MI355X HBM3E peak
 CALIB_COPY_BYTES = 512 << 20        # plain device copy whose counters calibrate FETCH/WRITE_SIZE
 ATTN_SOURCE = os.path.join(ROOT, "exact_head_attention_amd", "csrc", "attn_fwd.hip")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
+SQ_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_sq_counters.txt")
+PEAK_CLOCK_GHZ = 2.4                # the clock the published MFMA peaks assume
 
 
 def source_digest(path=ATTN_SOURCE):
@@ -59,6 +61,31 @@ def read_counter_summary(workload):
         write_scale = CALIB_COPY_BYTES / (float(kv["copy_write_kib"]) * 1024)
         return (float(kv["attn_fetch_kib"]) * 1024 * fetch_scale
                 + float(kv["attn_write_kib"]) * 1024 * write_scale)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _summary_kv(path):
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    return kv
+
+
+def read_sclk_summary(workload):
+    """Shader clock (GHz) the attention's full-round launch ran at, from the
+    committed SQ counter summary (SQ_BUSY_CYCLES per shader engine over the
+    dispatch's duration), or None when it is missing, for another workload or
+    for another kernel source than the one built now."""
+    try:
+        kv = _summary_kv(SQ_SUMMARY)
+        if kv.get("attn_source_sha256") != source_digest() or kv.get("workload") != workload:
+            return None
+        return float(kv["sclk_ghz"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -452,6 +479,13 @@ def main():
                      "frac_cold": round(pbytes / (pro_cold_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": pbytes},
     }
+    sclk = read_sclk_summary(w.name)
+    if sclk is not None:
+        # The published peak assumes 2.4 GHz; the chip holds a lower clock
+        # under this load (measured with counters, see the SQ summary).
+        rec["roofline"]["measured_sclk_ghz"] = sclk
+        rec["roofline"]["frac_at_measured_sclk"] = round(
+            att_tflops / (BF16_MFMA_PEAK_TFLOPS * sclk / PEAK_CLOCK_GHZ), 4)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
