@@ -300,8 +300,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // Slot (kt+3) % kSlots last held tile kt-1, whose K was read for the
   // scores of step kt-2 and whose V for the P.V of step kt-1, both before
   // the barrier that ended step kt-1.  R = kt % kSlots, a compile-time value.
-  auto step = [&](auto r_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    constexpr int R = decltype(r_c)::value;
+  auto step = [&](auto r_c, auto mask_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int R = decltype(r_c)::value;   // mask_c: whether tile kt+1 may hold keys past Lk
     // K tile kt+1 and V tile kt are visible since the barrier that ended the
     // previous step: the first score fragments are read before the ballot,
     // and the first P.V fragments late in the score phase, so neither read's
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     // (3) pw[4*(2b+t) + 0..3] holds the bf16 weights of keys 32b + 16t + 8g
     // + 0..7, the same keys the transposed V reads deliver for k-step
     // bt = 2b + t.  V fragments are read one k-step ahead (ping-pong).
-    mask_tile(s_nxt, kt + 1);
+    if constexpr (decltype(mask_c)::value) mask_tile(s_nxt, kt + 1);
     const float mx_next = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
@@ -392,11 +392,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     __syncthreads();
   };
 
-  for (int kt = 0; kt < n_steps; kt += kSlots) {
-    step(std::integral_constant<int, 0>{}, kt, s_a, s_b);
-    step(std::integral_constant<int, 1>{}, kt + 1, s_b, s_a);
-    step(std::integral_constant<int, 2>{}, kt + 2, s_a, s_b);
-    step(std::integral_constant<int, 3>{}, kt + 3, s_b, s_a);
+  // Groups of steps whose scored tiles (kt+1 .. kt+4) are all whole run
+  // without the mask.  A data-dependent branch inside a step splits it into
+  // basic blocks that the compiler schedules apart: it then sinks the
+  // exponentials below the score products instead of interleaving them
+  // (measured: 3% for the full-round launch, 5% for the tail launch).
+  const std::integral_constant<bool, true> masked{};
+  const std::integral_constant<bool, false> plain{};
+  int kt = 0;
+  for (; (kt + 5) * kBc <= Lk; kt += kSlots) {
+    step(std::integral_constant<int, 0>{}, plain, kt, s_a, s_b);
+    step(std::integral_constant<int, 1>{}, plain, kt + 1, s_b, s_a);
+    step(std::integral_constant<int, 2>{}, plain, kt + 2, s_a, s_b);
+    step(std::integral_constant<int, 3>{}, plain, kt + 3, s_b, s_a);
+  }
+  for (; kt < n_steps; kt += kSlots) {
+    step(std::integral_constant<int, 0>{}, masked, kt, s_a, s_b);
+    step(std::integral_constant<int, 1>{}, masked, kt + 1, s_b, s_a);
+    step(std::integral_constant<int, 2>{}, masked, kt + 2, s_a, s_b);
+    step(std::integral_constant<int, 3>{}, masked, kt + 3, s_b, s_a);
   }
   // Loads of tiles past the end are still in flight: they must land before
   // the workgroup's LDS is released.
