@@ -12,9 +12,9 @@
 //   * Keys stream in tiles of 64 through a 4-slot LDS ring per tensor, K and
 //     V both row-major [key][d] with an XOR swizzle of the 16-byte chunks.
 //     Tiles move from global memory straight into LDS (buffer loads with the
-//     LDS-destination bit), three tiles ahead of the one being multiplied,
-//     so no registers stage them and a load has two steps to land.  V is
-//     read as the transposed MFMA operand with ds_read_b64_tr_b16.
+//     LDS-destination bit), K three tiles and V two tiles ahead of their
+//     use, so no registers stage them and a load has two steps to land.  V
+//     is read as the transposed MFMA operand with ds_read_b64_tr_b16.
 //   * Per wave and key tile, with v_mfma_f32_32x32x16_bf16:
 //       S^T (64 keys x 32 queries) = K_tile . Q^T        16 MFMAs, Q^T in VGPRs
 //       O^T (128 d  x 32 queries) += V_tile^T . P^T      16 MFMAs
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
                    : "memory");
     }
   };
-  // Tiles are loaded V first, then K (2 kDma instructions per wave).  Waiting
-  // until at most one tile's loads are outstanding completes all older ones.
+  // Each step issues kDma loads of V and then kDma of K.  Waiting until at
+  // most one step's loads are outstanding completes all older ones.
   auto dma_pair = [&](int t) {
     dma_tile(Vh, t, v_lds[t % kSlots], false);
     dma_tile(Kh, t, k_lds[t % kSlots], true);
@@ -225,10 +225,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // constant; the up to kSlots-1 extra tiles lie wholly past Lk, so their
   // weights are exactly 0 and their (zero-filled) V rows add exact zeros.
   const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;
-  dma_pair(0);
-  dma_pair(1);
-  dma_pair(2);
-  dma_wait_all_but_one_pair();   // tiles 0 and 1 are in LDS (this wave's share)
+  dma_tile(Vh, 0, v_lds[0], false);
+  dma_tile(Kh, 0, k_lds[0], true);
+  dma_tile(Kh, 1, k_lds[1], true);
+  dma_tile(Vh, 1, v_lds[1], false);
+  dma_tile(Kh, 2, k_lds[2], true);
+  dma_wait_all_but_one_pair();   // K tiles 0, 1 and V tile 0 are in LDS (this wave's share)
   __syncthreads();
 
   // K fragment of chunk pair c: row krow (+32 for the second key block),
@@ -292,14 +294,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // their shadow, so the two waves sharing a SIMD (kept in step by the
   // barrier) leave the matrix pipe idle only around that barrier:
   //   (1) raise the running max if tile kt's max (found last step) exceeds it;
-  //   (2) the loads of tile kt+3 into ring slot (kt+3) % kSlots, then the
-  //       scores of tile kt+1 on the matrix cores, interleaved with tile kt's
-  //       exponentials;
+  //   (2) the loads of V tile kt+2 and K tile kt+3 into their ring slots,
+  //       then the scores of tile kt+1 on the matrix cores, interleaved with
+  //       tile kt's exponentials;
   //   (3) O += P.V for tile kt, interleaved with tile kt+1's row max;
-  //   (4) wait for this wave's loads of tile kt+2, then the barrier.
-  // Slot (kt+3) % kSlots last held tile kt-1, whose K was read for the
-  // scores of step kt-2 and whose V for the P.V of step kt-1, both before
-  // the barrier that ended step kt-1.  R = kt % kSlots, a compile-time value.
+  //   (4) wait for this wave's loads of V tile kt+1 and K tile kt+2 (issued
+  //       one step earlier), then the barrier.
+  // V slot (kt+2) % kSlots last held V tile kt-2 (read in step kt-2) and K
+  // slot (kt+3) % kSlots K tile kt-1 (read for the scores of step kt-2).
+  // Each wave's LDS reads of step j have completed once it is past the
+  // barrier ending step j (the wait right after it), so both slots are free
+  // two barriers after their last reads.  The barrier itself therefore waits
+  // for no LDS read: it is a bare s_barrier (with a compiler memory fence),
+  // and the compiler's own full LDS wait before it, which would stall on the
+  // P.V reads just issued, is avoided.  R = kt % kSlots, a compile-time value.
   auto step = [&](auto r_c, auto mask_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     constexpr int R = decltype(r_c)::value;   // mask_c: whether tile kt+1 may hold keys past Lk
     // K tile kt+1 and V tile kt are visible since the barrier that ended the
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const float neg_m = -m_run;
 
     // (2) K fragments are read one MFMA pair ahead (ping-pong registers).
-    dma_tile(Vh, kt + 3, v_lds[(R + 3) % kSlots], false);
+    dma_tile(Vh, kt + 2, v_lds[(R + 2) % kSlots], false);
     dma_tile(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
     uint32_t pw[16];
 #pragma unroll
@@ -389,7 +397,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     mx = mx_next;
     // (4)
     dma_wait_all_but_one_pair();
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
+    // This wave's P.V reads of this step land here at the latest, whatever
+    // the compiler does with the products that consume them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
   // Groups of steps whose scored tiles (kt+1 .. kt+4) are all whole run
