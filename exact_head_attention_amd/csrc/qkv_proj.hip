@@ -10,10 +10,12 @@
 // the norm.  Outputs are [H][L][128] bf16, the layout the attention reads.
 //
 // Work decomposition
-//   * Workgroup = (feature tile, token tile): two head slots (256 output
-//     features; slot j of the 3H q, k, v heads) x 256 tokens; 8 waves, each
-//     one head slot (128 features) x 64 tokens with its 8 accumulator tiles
-//     (128 registers): two waves per SIMD.
+//   * Workgroup = (feature tile, token tile): head slots (128 output
+//     features each; slot j of the 3H q, k, v heads) x 256 tokens, four
+//     waves per head slot, each one head slot x 64 tokens with its 8
+//     accumulator tiles (128 registers).  bf16 takes three head slots (12
+//     waves, three per SIMD); fp8, whose fragments need more registers,
+//     takes two (8 waves, two per SIMD).
 //   * The product is computed transposed, C^T = W . X^T, with
 //     v_mfma_f32_32x32x16_bf16: A = weight rows (features), B = hidden rows
 //     (tokens).  Both operands are K-contiguous in memory, so every fragment
@@ -23,8 +25,8 @@
 //     pair (2j, 2j+1) sits in one lane.
 //   * The hidden dimension streams in steps of 64 bytes per row (32 bf16 or
 //     64 fp8 elements) through a 4-slot LDS ring: buffer loads with the
-//     LDS-destination bit put each step's 256 weight rows and 256 token rows
-//     in LDS three steps ahead, with no register staging.  Rows are 64 bytes
+//     LDS-destination bit put each step's weight rows and 256 token rows in
+//     LDS three steps ahead, with no register staging.  Rows are 64 bytes
 //     with their four 16-byte chunks swizzled by (row / 4) % 4, so the 16
 //     rows of a fragment read hit 16 distinct bank groups.  The descriptor
 //     ranges make the last partial token tile (and an odd 3H's empty head
@@ -56,21 +58,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = kHeadDim;          // features per head slot
-constexpr int kSlots = 2;            // head slots (of the 3H q, k, v heads) per workgroup
 constexpr int kTok = 256;            // tokens per workgroup
-#ifndef H3_QKV_THREADS
-#define H3_QKV_THREADS 512
-#endif
-constexpr int kThreads = H3_QKV_THREADS;   // waves (slot, token range): 2 slots x kThreads/128 token ranges
-constexpr int kTS = 1024 / kThreads;       // 32-token sub-tiles per wave
-constexpr int kRows = kSlots * D;    // weight rows per workgroup
+constexpr int kTS = 2;               // 32-token sub-tiles per wave (64 tokens)
+constexpr int kTokRanges = kTok / (32 * kTS);   // waves per head slot
+// Head slots (of the 3H q, k, v heads) per workgroup: 3 for bf16 (12 waves,
+// three per SIMD: the bf16 form fits the 168 registers that allows), 2 for
+// fp8 (8 waves; its 32-byte fragments need more registers).
+template <bool kFp8> constexpr int slots_of() { return kFp8 ? 2 : 3; }
+template <bool kFp8> constexpr int threads_of() { return 64 * kTokRanges * slots_of<kFp8>(); }
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kStepBytes = 64;       // bytes of each row per step (32 bf16 or 64 fp8 hidden elements)
 constexpr int kRowElems = kStepBytes / 2;   // uint16 per LDS row (no padding)
 constexpr int kRing = 4;             // LDS ring depth (steps) for each of W and X
-constexpr int kWaves = kThreads / 64;
-constexpr int kDmaPerStep = 2 * 16 / kWaves;   // 1 KB loads per wave per step (W and X, 16 KB each)
 constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -111,12 +111,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // scales *x_scale and *w_scale (device scalars).  C counts hidden elements.
 // Head slot j in [0, 3H) is q head j, k head j - H or v head j - 2H.
 template <bool kFp8>
-__global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
+__global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void qkv_proj_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ Wq, const uint8_t *__restrict__ Wk,
     const uint8_t *__restrict__ Wv, const float *__restrict__ x_scale, const float *__restrict__ w_scale,
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
+  constexpr int kSlots = slots_of<kFp8>();
+  constexpr int kWaves = threads_of<kFp8>() / 64;
+  constexpr int kRows = kSlots * D;          // weight rows per workgroup
+  constexpr int kXLoads = kTok / 16;         // 1 KB loads per step for the token rows
   __shared__ __attribute__((aligned(1024))) uint16_t w_lds[kRing][kRows * kRowElems];
   __shared__ __attribute__((aligned(1024))) uint16_t x_lds[kRing][kTok * kRowElems];
 
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
   // Steps go from global memory straight into LDS (buffer loads with the
   // LDS-destination bit), three steps ahead of the one being multiplied.
   // Load j of wave w writes rows 16n .. 16n+15 (n = w + kWaves j) of the
-  // step's 256 weight rows or 256 token rows as one contiguous kilobyte: lane
+  // step's weight rows or 256 token rows as one contiguous kilobyte: lane
   // i lands in row 16n + i/4 at physical chunk i%4 and fetches the row's
   // logical chunk (i%4) ^ swizzle.  Rows past 3H or past L read as zeros
   // (descriptor range).  The waits below are explicit.
@@ -159,41 +163,54 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
   const int dma_row = lane >> 2;
   auto dma_step = [&](int ks, int slot) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
+    // Weight rows: waves 0..7 load 16-row block w of every head slot.
+    if (wave_u < 8u) {
 #pragma unroll
-    for (int j = 0; j < 16 / kWaves; ++j) {
-      const int n = wave + kWaves * j;          // weight rows 16n.., head slot n / 8
-      const int row = 16 * n + dma_row;
-      const int ch = (lane & 3) ^ row_swz(row);
-      const uint32_t m0 = lds_addr(w_lds[slot]) + (wave_u + kWaves * j) * 1024u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :
-                   : "s"(m0), "v"((row & (D - 1)) * row_bytes + kb + 16 * ch), "s"(rw[(kWaves * j) / 8])
-                   : "memory");
+      for (int h = 0; h < kSlots; ++h) {
+        const int row = 16 * wave + dma_row;    // row within head slot h
+        const int ch = (lane & 3) ^ row_swz(row);
+        const uint32_t m0 = lds_addr(w_lds[slot]) + (8u * h + wave_u) * 1024u;
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rw[h])
+                     : "memory");
+      }
     }
+    // Token rows: 16 blocks of 16, two per wave with 8 waves, or four per
+    // wave for waves 8..11 with 12.
+    constexpr int kXFirst = kWaves == 8 ? 0 : 8;
+    constexpr int kXWaves = kWaves - kXFirst;
+    if (wave_u >= static_cast<uint32_t>(kXFirst)) {
 #pragma unroll
-    for (int j = 0; j < 16 / kWaves; ++j) {
-      const int row = 16 * (wave + kWaves * j) + dma_row;
-      const int ch = (lane & 3) ^ row_swz(row);
-      const uint32_t m0 = lds_addr(x_lds[slot]) + (wave_u + kWaves * j) * 1024u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :
-                   : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rx)
-                   : "memory");
+      for (int j = 0; j < kXLoads / kXWaves; ++j) {
+        const uint32_t nu = wave_u - kXFirst + kXWaves * j;
+        const int row = 16 * (wave - kXFirst + kXWaves * j) + dma_row;
+        const int ch = (lane & 3) ^ row_swz(row);
+        const uint32_t m0 = lds_addr(x_lds[slot]) + nu * 1024u;
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rx)
+                     : "memory");
+      }
     }
   };
-  // Wait until this wave's loads of every step but the last `ahead` issued
-  // have landed.
+  // This wave's loads per step: kSlots of weight rows (waves 0..7) plus its
+  // token-row loads.
+  const int per_step = (wave_u < 8u ? kSlots : 0) +
+                       (wave_u >= static_cast<uint32_t>(kWaves == 8 ? 0 : 8) ? kXLoads / (kWaves == 8 ? 8 : 4) : 0);
+  static_assert(kWaves == 8 || kWaves == 12, "load split above");
   auto dma_wait = [&](int ahead) {
     if (ahead >= 2) {
-      if constexpr (kDmaPerStep == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      // Two steps' loads may stay outstanding (3 or 4 per step and wave).
+      if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
 
   // Wave (sl, th): head slot sl of the tile, tokens 32 kTS th .. + 32 kTS - 1.
-  const int sl = wave & 1, th = wave >> 1;
+  const int sl = wave % kSlots, th = wave / kSlots;
   f32x16 acc[4][kTS];
 #pragma unroll
   for (int fs = 0; fs < 4; ++fs)
@@ -324,8 +341,9 @@ __global__ __launch_bounds__(kThreads, kThreads / 256) void qkv_proj_kernel(
 
 }  // namespace
 
+// The larger of the two forms' grids (fp8: two head slots per workgroup).
 int64_t qkv_proj_grid(int H, int L) {
-  return ((static_cast<int64_t>(3) * H + kSlots - 1) / kSlots) * ((static_cast<int64_t>(L) + kTok - 1) / kTok);
+  return ((static_cast<int64_t>(3) * H + 1) / 2) * ((static_cast<int64_t>(L) + kTok - 1) / kTok);
 }
 
 hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, const uint16_t *wk,
@@ -333,8 +351,8 @@ hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, co
                                        const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k,
                                        uint16_t *v, int H, int L, int C, float eps, hipStream_t stream) {
   const int n_ttiles = (L + kTok - 1) / kTok;
-  const int blocks = static_cast<int>(qkv_proj_grid(H, L));
-  hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream,
+  const int blocks = (3 * H + slots_of<false>() - 1) / slots_of<false>() * n_ttiles;
+  hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3(blocks), dim3(threads_of<false>()), 0, stream,
                      reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(wq),
                      reinterpret_cast<const uint8_t *>(wk), reinterpret_cast<const uint8_t *>(wv), nullptr, nullptr,
                      gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
@@ -347,8 +365,8 @@ hipError_t launch_qkv_proj_fp8_qknorm_rope(const uint8_t *x, const float *x_scal
                                            const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *v, int H, int L,
                                            int C, float eps, hipStream_t stream) {
   const int n_ttiles = (L + kTok - 1) / kTok;
-  const int blocks = static_cast<int>(qkv_proj_grid(H, L));
-  hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, x, wq, wk, wv, x_scale,
+  const int blocks = (3 * H + slots_of<true>() - 1) / slots_of<true>() * n_ttiles;
+  hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3(blocks), dim3(threads_of<true>()), 0, stream, x, wq, wk, wv, x_scale,
                      w_scale, gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
   return hipGetLastError();
 }
