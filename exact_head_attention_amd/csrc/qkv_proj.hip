@@ -11,11 +11,12 @@
 //
 // Work decomposition
 //   * Workgroup = (feature tile, token tile): head slots (128 output
-//     features each; slot j of the 3H q, k, v heads) x 256 tokens, four
-//     waves per head slot, each one head slot x 64 tokens with its 8
-//     accumulator tiles (128 registers).  bf16 takes three head slots (12
-//     waves, three per SIMD); fp8, whose fragments need more registers,
-//     takes two (8 waves, two per SIMD).
+//     features each; slot j of the 3H q, k, v heads) x 256 tokens.  bf16:
+//     three head slots, 12 waves (three per SIMD), each one head slot x 64
+//     tokens with 8 accumulator tiles.  fp8, whose 32-byte fragments leave
+//     no room for that at three waves per SIMD: two head slots, 16 waves
+//     (four per SIMD), each one head slot x 32 tokens with 4 accumulator
+//     tiles.
 //   * The product is computed transposed, C^T = W . X^T, with
 //     v_mfma_f32_32x32x16_bf16: A = weight rows (features), B = hidden rows
 //     (tokens).  Both operands are K-contiguous in memory, so every fragment
@@ -59,13 +60,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int D = kHeadDim;          // features per head slot
 constexpr int kTok = 256;            // tokens per workgroup
-constexpr int kTS = 2;               // 32-token sub-tiles per wave (64 tokens)
-constexpr int kTokRanges = kTok / (32 * kTS);   // waves per head slot
-// Head slots (of the 3H q, k, v heads) per workgroup: 3 for bf16 (12 waves,
-// three per SIMD: the bf16 form fits the 168 registers that allows), 2 for
-// fp8 (8 waves; its 32-byte fragments need more registers).
+// 32-token sub-tiles per wave: 2 (64 tokens) for bf16, 1 for fp8.
+template <bool kFp8> constexpr int ts_of() { return kFp8 ? 1 : 2; }
+template <bool kFp8> constexpr int ranges_of() { return kTok / (32 * ts_of<kFp8>()); }   // waves per head slot
+// Head slots (of the 3H q, k, v heads) per workgroup: 3 for bf16 (12 waves
+// of 64 tokens, three per SIMD: the bf16 form fits the 168 registers that
+// allows), 2 for fp8 (16 waves of 32 tokens, four per SIMD, within 128).
 template <bool kFp8> constexpr int slots_of() { return kFp8 ? 2 : 3; }
-template <bool kFp8> constexpr int threads_of() { return 64 * kTokRanges * slots_of<kFp8>(); }
+template <bool kFp8> constexpr int threads_of() { return 64 * ranges_of<kFp8>() * slots_of<kFp8>(); }
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kStepBytes = 64;       // bytes of each row per step (32 bf16 or 64 fp8 hidden elements)
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
     uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
   constexpr int kSlots = slots_of<kFp8>();
+  constexpr int kTS = ts_of<kFp8>();
   constexpr int kWaves = threads_of<kFp8>() / 64;
   constexpr int kRows = kSlots * D;          // weight rows per workgroup
   constexpr int kXLoads = kTok / 16;         // 1 KB loads per step for the token rows
@@ -161,6 +164,9 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
   // (descriptor range).  The waits below are explicit.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int dma_row = lane >> 2;
+  // Token-row loads: all waves with 8, waves 8.. with 12 or 16.
+  constexpr int kXFirst = kWaves == 8 ? 0 : 8;
+  constexpr int kXWaves = kWaves - kXFirst;
   auto dma_step = [&](int ks, int slot) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
     // Weight rows: waves 0..7 load 16-row block w of every head slot.
@@ -178,8 +184,6 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
     }
     // Token rows: 16 blocks of 16, two per wave with 8 waves, or four per
     // wave for waves 8..11 with 12.
-    constexpr int kXFirst = kWaves == 8 ? 0 : 8;
-    constexpr int kXWaves = kWaves - kXFirst;
     if (wave_u >= static_cast<uint32_t>(kXFirst)) {
 #pragma unroll
       for (int j = 0; j < kXLoads / kXWaves; ++j) {
@@ -196,13 +200,14 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
   };
   // This wave's loads per step: kSlots of weight rows (waves 0..7) plus its
   // token-row loads.
-  const int per_step = (wave_u < 8u ? kSlots : 0) +
-                       (wave_u >= static_cast<uint32_t>(kWaves == 8 ? 0 : 8) ? kXLoads / (kWaves == 8 ? 8 : 4) : 0);
-  static_assert(kWaves == 8 || kWaves == 12, "load split above");
+  const int per_step = (wave_u < 8u ? kSlots : 0) + (wave_u >= static_cast<uint32_t>(kXFirst) ? kXLoads / kXWaves : 0);
+  static_assert(kWaves == 8 || kWaves == 12 || kWaves == 16, "load split above");
   auto dma_wait = [&](int ahead) {
     if (ahead >= 2) {
-      // Two steps' loads may stay outstanding (3 or 4 per step and wave).
-      if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      // Two steps' loads may stay outstanding (3 or 4 per step and wave with
+      // 8 or 12 waves, 2 with 16).
+      if constexpr (kWaves == 16) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
