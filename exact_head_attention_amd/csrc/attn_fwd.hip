@@ -185,6 +185,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // chunk (i%16) ^ swizzle.  Keys at or past Lk read as zeros (the
   // descriptor covers only the tile's valid rows).  The loads are tracked by
   // the vector-memory counter only; the waits below are explicit.
+  // Each load sets m0 (its LDS destination) itself.  m0 cannot be named as
+  // clobbered (the compiler reserves it); no compiler-generated instruction
+  // in this kernel reads or writes it.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto dma_tile = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
     const int keys_left = Lk - t * kBc;

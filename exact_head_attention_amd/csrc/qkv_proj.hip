@@ -162,6 +162,9 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
   // i lands in row 16n + i/4 at physical chunk i%4 and fetches the row's
   // logical chunk (i%4) ^ swizzle.  Rows past 3H or past L read as zeros
   // (descriptor range).  The waits below are explicit.
+  // Each load sets m0 (its LDS destination) itself.  m0 cannot be named as
+  // clobbered (the compiler reserves it); no compiler-generated instruction
+  // in this kernel reads or writes it.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int dma_row = lane >> 2;
   // Token-row loads: all waves with 8, waves 8.. with 12 or 16.
