@@ -108,7 +108,7 @@ def summarize(args):
         call_us = 0.0
         for r in rows:
             name = _kernel_short(r["Name"])
-            if name.startswith("attn_fwd_kernel<") and name.endswith("false>"):
+            if name in ("attn_fwd_kernel<false>", "attn_tail_kernel<false>"):
                 call_us += float(r["AverageNs"]) / 1e3
             if "reduce_kernel" in r["Name"]:
                 name = "torch amax (read-only cache flush)"
@@ -120,15 +120,15 @@ def summarize(args):
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
         if call_us > 0:
-            out.append(f"# one h3_attention call = attn_fwd_kernel<8, false> (full rounds) + "
-                       f"attn_fwd_kernel<4, false> (tail, when launched): {call_us:.2f} us per call")
+            out.append(f"# one h3_attention call = attn_fwd_kernel<false> (full rounds) + "
+                       f"attn_tail_kernel<false> (tail, when launched): {call_us:.2f} us per call")
     if args.pmc:
         per = {}
         for d in args.pmc:
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
-                    key = ("attn_main" if "attn_fwd_kernel<8, false>" in r["Kernel_Name"] else
-                           "attn_tail" if "attn_fwd_kernel<4, false>" in r["Kernel_Name"] else
+                    key = ("attn_main" if "attn_fwd_kernel<false>" in r["Kernel_Name"] else
+                           "attn_tail" if "attn_tail_kernel<false>" in r["Kernel_Name"] else
                            "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
                         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))

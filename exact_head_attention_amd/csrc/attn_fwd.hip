@@ -8,7 +8,8 @@
 // Work decomposition
 //   * Work unit = one (head, 256-query tile); each wave owns 32 query rows.
 //     A unit runs as one 8-wave workgroup, or, in the tail launch, as two
-//     4-wave workgroups of 128 rows each (see launch_split below).
+//     8-wave workgroups of 128 rows each in which two waves share each 32-row
+//     group (attn_tail_kernel; see launch_split below).
 //   * Keys stream in tiles of 64 through a 4-slot LDS ring per tensor, K and
 //     V both row-major [key][d] with an XOR swizzle of the 16-byte chunks.
 //     Tiles move from global memory straight into LDS (buffer loads with the
@@ -30,9 +31,10 @@
 //     as e^(scale*s - m') with m' = m / log2(e).
 //
 // Determinism: a row's arithmetic depends only on its (head, row) and keys
-// are visited in a fixed order; 8- and 4-wave workgroups run the same per-wave
-// code and differ only in how many tile loads each wave issues.  So every
-// head's output is bit-identical however many heads one launch covers.
+// are visited in a fixed order; the tail kernel performs each row's
+// operations in the same order as the main kernel, only split over two
+// waves.  So every head's output is bit-identical however many heads one
+// launch covers.
 // The XCD-aware block remap and the main/tail split change only where and
 // when a row runs.
 #include <hip/hip_runtime.h>
@@ -129,23 +131,129 @@ __device__ __forceinline__ float max32(const f32x16 &a, const f32x16 &b) {
   return t[0];
 }
 
+constexpr int kWaves = 8;   // waves per workgroup in both kernels
+
+// Wave `wave` (of 8) moves its two 1-KB pieces of 64-key tile t of one
+// tensor from global memory straight into LDS (buffer loads with the
+// LDS-destination bit).  Piece j covers rows 4n .. 4n+3, n = wave + 8j, as
+// one contiguous kilobyte: lane i lands in row 4n + i/16 at physical chunk
+// i%16, so it fetches the row's logical chunk (i%16) ^ swizzle.  Keys at or
+// past Lk read as zeros (the descriptor covers only the tile's valid rows).
+// The loads are tracked by the vector-memory counter only; callers wait
+// explicitly.  Each load sets m0 (its LDS destination) itself.  m0 cannot be
+// named as clobbered (the compiler reserves it); no compiler-generated
+// instruction in these kernels reads or writes it.
+__device__ __forceinline__ void dma_tile(const uint16_t *base, int t, int Lk, const uint16_t *dst, bool is_k,
+                                         int wave, uint32_t wave_u, int lane) {
+  const int keys_left = Lk - t * kBc;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * (D * 2));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = wave + kWaves * j;
+    const int row = 4 * n + (lane >> 4);
+    const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
+    const uint32_t m0 = lds_addr(dst) + (wave_u + kWaves * j) * 1024u;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(row * (D * 2) + 16 * chunk), "s"(rs)
+                 : "memory");
+  }
+}
+
+// K fragment of chunk pair c (A operand of the score product): row krow
+// (+32 for the second key block), logical chunk 2c + g, i.e. physical chunk
+// 2c ^ (g ^ (krow & 15)), krow = l32 with bits 2 and 3 swapped.
+__device__ __forceinline__ void k_offsets(int lane, int (&koff)[8]) {
+  const int krow = swap_bits23(lane & 31), g = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) koff[c] = krow * D + 8 * ((2 * c) ^ (g ^ k_swz(krow)));
+}
+__device__ __forceinline__ bf16x8 kread(const uint16_t *kt_lds, const int (&koff)[8], int b, int c) {
+  return *reinterpret_cast<const bf16x8 *>(kt_lds + koff[c] + b * 32 * D);
+}
+
+// Transposed V reads: within each 16-lane group, lane L names row
+// 8g + L/4 (+4 for the second read) and columns 16*dhalf + 4*(L%4) .. +3;
+// the hardware hands lane j of the group column 16*dhalf + j of the four
+// named rows, i.e. V[8g + 0..7][32db + l32] across the two reads.
+// The columns of d block db sit in logical chunk 4db + 2 dhalf + (L%4)/2 of
+// rows 8g + L/4 (+16 per k-step, +4 for the second read), whose swizzle
+// 4 (row & 3) depends on L only.
+__device__ __forceinline__ void v_offsets(int lane, int (&voff)[4]) {
+  const int g = lane >> 5;
+  const int vrow = 8 * g + ((lane & 15) >> 2);
+  const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) voff[db] = vrow * D + 8 * ((4 * db + vch) ^ v_swz(vrow)) + 4 * (lane & 1);
+}
+__device__ __forceinline__ bf16x8 vread(const uint16_t *vt, const int (&voff)[4], int bt, int db) {
+  const uint16_t *src = vt + voff[db] + 16 * bt * D;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * D));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Mask the keys of tile t at or past Lk (only the last, ragged tile has any).
+// s[b][i] holds key t*64 + 32b + 16(i/8) + 8g + i%8.
+__device__ __forceinline__ void mask_tile(f32x16 (&sv)[2], int t, int Lk, int g) {
+  const int key_base = t * kBc;
+  if (key_base + kBc > Lk) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= Lk) sv[b][i] = -__builtin_inff();
+  }
+}
+
+// Epilogue of one lane's half of query row qrow: normalise by the full row
+// sum and round once to bf16 (or keep fp32 and write the log-sum-exp:
+// ln(l * 2^m) = (log2(l) + m) * ln 2).  o[db][4*grp + r] holds
+// d = 32db + 8grp + 4g + r.
+template <bool kLse>
+__device__ __forceinline__ void store_row(const f32x16 (&o)[4], float l_tot, float m_run, size_t head_off, int head,
+                                          int qrow, int Lq, int g, uint16_t *O, float *O32, float *lse_out) {
+  const float inv_l = 1.0f / l_tot;
+  if (kLse && qrow < Lq) {
+    float *orow = O32 + head_off + static_cast<size_t>(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        *reinterpret_cast<float4 *>(orow + 32 * db + 8 * grp + 4 * g) =
+            make_float4(o[db][4 * grp + 0] * inv_l, o[db][4 * grp + 1] * inv_l, o[db][4 * grp + 2] * inv_l,
+                        o[db][4 * grp + 3] * inv_l);
+    if (g == 0)
+      lse_out[static_cast<size_t>(head) * Lq + qrow] = (__builtin_amdgcn_logf(l_tot) + m_run) * 0.69314718055994531f;
+  }
+  if (!kLse && qrow < Lq) {
+    uint16_t *orow = O + head_off + static_cast<size_t>(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        uint2 w;
+        w.x = pack_bf16x2(o[db][4 * grp + 0] * inv_l, o[db][4 * grp + 1] * inv_l);
+        w.y = pack_bf16x2(o[db][4 * grp + 2] * inv_l, o[db][4 * grp + 3] * inv_l);
+        *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * grp + 4 * g) = w;
+      }
+  }
+}
+
 // kLse = false: out = softmax(scale q k^T) v rounded to bf16 (h3_attention).
 // kLse = true:  out_f32 = the same normalised result in fp32 and lse = the
 // natural log of sum_j exp(scale q.k_j) over the Lk keys given (the partial
 // form h3_attention_merge combines).  Queries: [H][Lq][D]; keys and values:
 // element (h, j, d) at h*kv_stride + j*D + d, j < Lk.
 //
-// NW waves per workgroup (8: one whole unit; 4: half a unit).  Block b covers
-// unit unit_base + r / (8/NW), part r % (8/NW), with r the XCD-remapped b.
-template <int NW, bool kLse>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
+// One 8-wave workgroup per unit: block b covers unit unit_base + r, with r
+// the XCD-remapped b.
+template <bool kLse>
+__global__ __launch_bounds__(512) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
     long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
-  constexpr int kThreads = NW * 64;
-  constexpr int kParts = 8 / NW;           // workgroups per unit
-  constexpr int kDma = 16 / NW;            // 1 KB DMA instructions per wave per tensor and tile
-  static_assert(NW == 8 || NW == 4, "8- or 4-wave workgroups");
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kSlots][kTileElems];
 
@@ -154,11 +262,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int l32 = lane & 31, g = lane >> 5;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = unit_base + logical / kParts;
+  const int unit = unit_base + logical;
   const int head = unit / n_qtiles;
   const int qt = unit - head * n_qtiles;
-  const int row0 = qt * kUnitRows + (logical % kParts) * (NW * 32);
-  if (row0 >= Lq) return;   // the empty half of a ragged last unit (uniform per block)
+  const int row0 = qt * kUnitRows;
   const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Qh = Q + head_off;
   const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
@@ -171,52 +278,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   {
     // Descriptor over this workgroup's rows only: sizes stay below 2^31 bytes
     // for any L the API accepts.
-    const int rows_left = Lq - row0 < NW * 32 ? Lq - row0 : NW * 32;
+    const int rows_left = Lq - row0 < kUnitRows ? Lq - row0 : kUnitRows;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh + static_cast<size_t>(row0) * D, rows_left * row_bytes);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, (wave * 32 + l32) * row_bytes + 32 * c + 16 * g));
   }
 
-  // Tiles go from global memory straight into LDS (buffer loads with the
-  // LDS-destination bit).  Instruction j of wave w writes rows
-  // 4n .. 4n+3, n = w + NW j, as one contiguous kilobyte: lane i lands in
-  // row 4n + i/16 at physical chunk i%16, so it fetches the row's logical
-  // chunk (i%16) ^ swizzle.  Keys at or past Lk read as zeros (the
-  // descriptor covers only the tile's valid rows).  The loads are tracked by
-  // the vector-memory counter only; the waits below are explicit.
-  // Each load sets m0 (its LDS destination) itself.  m0 cannot be named as
-  // clobbered (the compiler reserves it); no compiler-generated instruction
-  // in this kernel reads or writes it.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto dma_tile = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    const int keys_left = Lk - t * kBc;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * row_bytes);
-#pragma unroll
-    for (int j = 0; j < kDma; ++j) {
-      const int n = wave + NW * j;
-      const int row = 4 * n + (lane >> 4);
-      const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
-      const uint32_t m0 = lds_addr(dst) + (wave_u + NW * j) * 1024u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :
-                   : "s"(m0), "v"(row * row_bytes + 16 * chunk), "s"(rs)
-                   : "memory");
-    }
+  auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
+    dma_tile(base, t, Lk, dst, is_k, wave, wave_u, lane);
   };
-  // Each step issues kDma loads of V and then kDma of K.  Waiting until at
+  // Each step issues two loads of V and then two of K.  Waiting until at
   // most one step's loads are outstanding completes all older ones.
-  auto dma_pair = [&](int t) {
-    dma_tile(Vh, t, v_lds[t % kSlots], false);
-    dma_tile(Kh, t, k_lds[t % kSlots], true);
-  };
-  auto dma_wait_all_but_one_pair = [&]() {
-    if constexpr (kDma == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  };
+  auto dma_wait_all_but_one_pair = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
 
-  const int krow = swap_bits23(l32);
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
@@ -228,55 +304,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // constant; the up to kSlots-1 extra tiles lie wholly past Lk, so their
   // weights are exactly 0 and their (zero-filled) V rows add exact zeros.
   const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;
-  dma_tile(Vh, 0, v_lds[0], false);
-  dma_tile(Kh, 0, k_lds[0], true);
-  dma_tile(Kh, 1, k_lds[1], true);
-  dma_tile(Vh, 1, v_lds[1], false);
-  dma_tile(Kh, 2, k_lds[2], true);
+  dma(Vh, 0, v_lds[0], false);
+  dma(Kh, 0, k_lds[0], true);
+  dma(Kh, 1, k_lds[1], true);
+  dma(Vh, 1, v_lds[1], false);
+  dma(Kh, 2, k_lds[2], true);
   dma_wait_all_but_one_pair();   // K tiles 0, 1 and V tile 0 are in LDS (this wave's share)
   __syncthreads();
 
-  // K fragment of chunk pair c: row krow (+32 for the second key block),
-  // logical chunk 2c + g, i.e. physical chunk 2c ^ (g ^ (krow & 15)).
-  int koff[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) koff[c] = krow * D + 8 * ((2 * c) ^ (g ^ k_swz(krow)));
-  // Transposed V reads: within each 16-lane group, lane L names row
-  // 8g + L/4 (+4 for the second read) and columns 16*dhalf + 4*(L%4) .. +3;
-  // the hardware hands lane j of the group column 16*dhalf + j of the four
-  // named rows, i.e. V[8g + 0..7][32db + l32] across the two reads.
-  // The columns of d block db sit in logical chunk 4db + 2 dhalf + (L%4)/2 of
-  // rows 8g + L/4 (+16 per k-step, +4 for the second read), whose swizzle
-  // 4 (row & 3) depends on L only.
-  int voff[4];
-  {
-    const int vrow = 8 * g + ((lane & 15) >> 2);
-    const int vch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) voff[db] = vrow * D + 8 * ((4 * db + vch) ^ v_swz(vrow)) + 4 * (lane & 1);
-  }
-  auto vread = [&](const uint16_t *vt, int bt, int db) {
-    const uint16_t *src = vt + voff[db] + 16 * bt * D;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * D));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto kread = [&](const uint16_t *kt_lds, int b, int c) {
-    return *reinterpret_cast<const bf16x8 *>(kt_lds + koff[c] + b * 32 * D);
-  };
-
-  // Mask the keys of tile t at or past Lk (only the last, ragged tile has any).
-  // s[b][i] holds key t*64 + 32b + 16(i/8) + 8g + i%8.
-  auto mask_tile = [&](f32x16 (&sv)[2], int t) {
-    const int key_base = t * kBc;
-    if (key_base + kBc > Lk) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key_base + 32 * b + 16 * (i >> 3) + 8 * g + (i & 7) >= Lk) sv[b][i] = -__builtin_inff();
-    }
-  };
+  int koff[8], voff[4];
+  k_offsets(lane, koff);
+  v_offsets(lane, voff);
 
   f32x16 s_a[2], s_b[2];
   {
@@ -284,11 +322,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     s_a[1] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], 0, c), qf[c], s_a[0], 0, 0, 0);
-      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], 1, c), qf[c], s_a[1], 0, 0, 0);
+      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], koff, 0, c), qf[c], s_a[0], 0, 0, 0);
+      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], koff, 1, c), qf[c], s_a[1], 0, 0, 0);
     }
   }
-  mask_tile(s_a, 0);
+  mask_tile(s_a, 0, Lk, g);
   // Row max (scaled, base 2) of the tile whose softmax the next step does.
   float mx = lane_half_max(max32(s_a[0], s_a[1])) * scale_log2e;
 
@@ -319,8 +357,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     // latency opens its phase.
     const uint16_t *kp = k_lds[(R + 1) % kSlots];
     bf16x8 ka[2][2];
-    ka[0][0] = kread(kp, 0, 0);
-    ka[0][1] = kread(kp, 1, 0);
+    ka[0][0] = kread(kp, koff, 0, 0);
+    ka[0][1] = kread(kp, koff, 1, 0);
     const uint16_t *vp = v_lds[R];
     bf16x8 vf[2][4];
     // (1)
@@ -338,18 +376,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const float neg_m = -m_run;
 
     // (2) K fragments are read one MFMA pair ahead (ping-pong registers).
-    dma_tile(Vh, kt + 2, v_lds[(R + 2) % kSlots], false);
-    dma_tile(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
+    dma(Vh, kt + 2, v_lds[(R + 2) % kSlots], false);
+    dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
     uint32_t pw[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int cur = c & 1, nxt = cur ^ 1;
       if (c < 7) {
-        ka[nxt][0] = kread(kp, 0, c + 1);
-        ka[nxt][1] = kread(kp, 1, c + 1);
+        ka[nxt][0] = kread(kp, koff, 0, c + 1);
+        ka[nxt][1] = kread(kp, koff, 1, c + 1);
       } else {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, 0, db);
+        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, voff, 0, db);
       }
       s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
@@ -377,14 +415,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     // (3) pw[4*(2b+t) + 0..3] holds the bf16 weights of keys 32b + 16t + 8g
     // + 0..7, the same keys the transposed V reads deliver for k-step
     // bt = 2b + t.  V fragments are read one k-step ahead (ping-pong).
-    if constexpr (decltype(mask_c)::value) mask_tile(s_nxt, kt + 1);
+    if constexpr (decltype(mask_c)::value) mask_tile(s_nxt, kt + 1, Lk, g);
     const float mx_next = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
       const int cur = bt & 1, nxt = cur ^ 1;
       if (bt < 3) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, bt + 1, db);
+        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, voff, bt + 1, db);
       }
       const uint4 w = make_uint4(pw[4 * bt], pw[4 * bt + 1], pw[4 * bt + 2], pw[4 * bt + 3]);
 #pragma unroll
@@ -431,34 +469,229 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const float l_run = l_run0 + l_run1;
 
-  // Epilogue: full row sum, normalise, round once to bf16 (or keep fp32 and
-  // write the log-sum-exp: ln(l * 2^m) = (log2(l) + m) * ln 2).
-  const float l_tot = lane_half_sum(l_run);
-  const float inv_l = 1.0f / l_tot;
-  if (kLse && qrow < Lq) {
-    float *orow = O32 + head_off + static_cast<size_t>(qrow) * D;
+  store_row<kLse>(o, lane_half_sum(l_run), m_run, head_off, head, qrow, Lq, g, O, O32, lse_out);
+}
+
+// Tail form: one 8-wave workgroup per 128 query rows (four 32-row groups).
+// Wave w < 4, the producer of group w, computes the scores, the running max
+// and sum and the bf16 weights P.  Wave w + 4, its consumer (placed on the
+// same SIMD), holds O and applies each tile's rescale and P.V one step
+// later, fed through LDS with P and the per-row factor alpha.  Every row
+// sees the same operations in the same order as in attn_fwd_kernel (an O
+// rescale by exactly 1 is an identity), so its bits do not change; the split
+// only gives each SIMD two waves where 128-row units would leave it one.
+//   Step kt: producers score tile kt+1 and weigh tile kt; consumers apply
+//   tile kt-1.  Every wave issues its share of V tile kt+1 (3-slot ring, read
+//   in step kt+2) and K tile kt+3 (4-slot ring, read in step kt+2), and waits
+//   for all its older loads before the step's barrier.  Every LDS access of a
+//   step has completed before that barrier (lgkmcnt(0)), so a slot may be
+//   rewritten from the step after its last read on.  K + V + P rings:
+//   64 + 48 + 32 KB.
+template <bool kLse>
+__global__ __launch_bounds__(512) void attn_tail_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
+    long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
+  constexpr int kVSlots = 3;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kVSlots][kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint4 p_lds[2][4][4 * 64];   // [slot][group][16 B piece j * 64 + lane]
+  __shared__ float a_lds[2][4][32];                                         // [slot][group][row]: alpha
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int grp = wave & 3;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = unit_base + (logical >> 1);
+  const int head = unit / n_qtiles;
+  const int qt = unit - head * n_qtiles;
+  const int row0 = qt * kUnitRows + (logical & 1) * 128;
+  if (row0 >= Lq) return;   // the empty half of a ragged last unit (uniform per block)
+  const size_t head_off = static_cast<size_t>(head) * Lq * D;
+  const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
+  const uint16_t *Vh = V + static_cast<size_t>(head) * kv_stride;
+  const int qrow = row0 + grp * 32 + l32;
+
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
+    dma_tile(base, t, Lk, dst, is_k, wave, wave_u, lane);
+  };
+  auto end_step = [&]() {
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");   // all but this step's 4 loads
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  const int n_kt = (Lk + kBc - 1) / kBc;
+  const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;   // as in attn_fwd_kernel
+  dma(Kh, 0, k_lds[0], true);
+  dma(Kh, 1, k_lds[1], true);
+  dma(Kh, 2, k_lds[2], true);
+  dma(Vh, 0, v_lds[0], false);
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // K tiles 0 and 1 (this wave's share)
+  __syncthreads();
+
+  if (wave_u < 4) {
+    // Producer: the first half of attn_fwd_kernel's step, P and alpha to LDS.
+    bf16x8 qf[8];
+    {
+      const int rows_left = Lq - row0 < 128 ? Lq - row0 : 128;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off + static_cast<size_t>(row0) * D, rows_left * (D * 2));
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int c = 0; c < 8; ++c)
+        qf[c] = __builtin_bit_cast(bf16x8, bload128(rq, (grp * 32 + l32) * (D * 2) + 32 * c + 16 * g));
+    }
+    int koff[8];
+    k_offsets(lane, koff);
+    float m_run = -__builtin_inff();
+    float l_run0 = 0.f, l_run1 = 0.f;
+    f32x16 s_a[2], s_b[2];
+    s_a[0] = f32x16{};
+    s_a[1] = f32x16{};
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp)
-        *reinterpret_cast<float4 *>(orow + 32 * db + 8 * grp + 4 * g) =
-            make_float4(o[db][4 * grp + 0] * inv_l, o[db][4 * grp + 1] * inv_l, o[db][4 * grp + 2] * inv_l,
-                        o[db][4 * grp + 3] * inv_l);
-    if (g == 0)
-      lse_out[static_cast<size_t>(head) * Lq + qrow] = (__builtin_amdgcn_logf(l_tot) + m_run) * 0.69314718055994531f;
-  }
-  if (!kLse && qrow < Lq) {
-    uint16_t *orow = O + head_off + static_cast<size_t>(qrow) * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        // o[db][4*grp + r] holds d = 32db + 8grp + 4g + r.
-        uint2 w;
-        w.x = pack_bf16x2(o[db][4 * grp + 0] * inv_l, o[db][4 * grp + 1] * inv_l);
-        w.y = pack_bf16x2(o[db][4 * grp + 2] * inv_l, o[db][4 * grp + 3] * inv_l);
-        *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * grp + 4 * g) = w;
+    for (int c = 0; c < 8; ++c) {
+      s_a[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], koff, 0, c), qf[c], s_a[0], 0, 0, 0);
+      s_a[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds[0], koff, 1, c), qf[c], s_a[1], 0, 0, 0);
+    }
+    mask_tile(s_a, 0, Lk, g);
+    float mx = lane_half_max(max32(s_a[0], s_a[1])) * scale_log2e;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    int vs = 1;   // V ring slot of tile kt + 1
+
+    auto pstep = [&](auto r_c, auto mask_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+      constexpr int R = decltype(r_c)::value;
+      const uint16_t *kp = k_lds[(R + 1) % kSlots];
+      bf16x8 ka[2][2];
+      ka[0][0] = kread(kp, koff, 0, 0);
+      ka[0][1] = kread(kp, koff, 1, 0);
+      float alpha = 1.0f;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
+        const float m_new = __builtin_fmaxf(m_run, mx);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run0 *= alpha;
+        l_run1 *= alpha;
       }
+      if (g == 0) a_lds[R & 1][grp][l32] = alpha;
+      const float neg_m = -m_run;
+      dma(Vh, kt + 1, v_lds[vs], false);
+      dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
+      vs = vs == kVSlots - 1 ? 0 : vs + 1;
+      uint32_t pw[16];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int cur = c & 1, nxt = cur ^ 1;
+        if (c < 7) {
+          ka[nxt][0] = kread(kp, koff, 0, c + 1);
+          ka[nxt][1] = kread(kp, koff, 1, c + 1);
+        }
+        s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int b = c >> 2, i = 4 * (c & 3) + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i], scale_log2e, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i + 1], scale_log2e, neg_m));
+          pw[2 * c + e] = pack_bf16x2(p0, p1);
+          if (e == 0)
+            l_run0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run0, false);
+          else
+            l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run1, false);
+        }
+        s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][1], qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
+        if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's K reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+      }
+      // pw[4j .. 4j+3] feeds the consumer's k-step j: lane-major 16-byte pieces.
+      uint4 *pd = &p_lds[R & 1][grp][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pd[64 * j] = make_uint4(pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]);
+      if constexpr (decltype(mask_c)::value) mask_tile(s_nxt, kt + 1, Lk, g);
+      mx = lane_half_max(max32(s_nxt[0], s_nxt[1])) * scale_log2e;
+      end_step();
+    };
+    const std::integral_constant<bool, true> masked{};
+    const std::integral_constant<bool, false> plain{};
+    int kt = 0;
+    for (; (kt + 5) * kBc <= Lk; kt += kSlots) {
+      pstep(std::integral_constant<int, 0>{}, plain, kt, s_a, s_b);
+      pstep(std::integral_constant<int, 1>{}, plain, kt + 1, s_b, s_a);
+      pstep(std::integral_constant<int, 2>{}, plain, kt + 2, s_a, s_b);
+      pstep(std::integral_constant<int, 3>{}, plain, kt + 3, s_b, s_a);
+    }
+    for (; kt < n_steps; kt += kSlots) {
+      pstep(std::integral_constant<int, 0>{}, masked, kt, s_a, s_b);
+      pstep(std::integral_constant<int, 1>{}, masked, kt + 1, s_b, s_a);
+      pstep(std::integral_constant<int, 2>{}, masked, kt + 2, s_a, s_b);
+      pstep(std::integral_constant<int, 3>{}, masked, kt + 3, s_b, s_a);
+    }
+    // The row's total and max for the consumer, in P slot 0 (n_steps is even,
+    // so slot 0 was last read in step n_steps - 1).
+    const float l_tot = lane_half_sum(l_run0 + l_run1);
+    float *ed = reinterpret_cast<float *>(&p_lds[0][grp][0]);
+    if (g == 0) {
+      ed[l32] = l_tot;
+      ed[32 + l32] = m_run;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+  } else {
+    // Consumer: O = O * alpha + P.V, one tile behind its producer.
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    int voff[4];
+    v_offsets(lane, voff);
+    auto apply = [&](int ps, const uint16_t *vp) {
+      const float alpha = a_lds[ps][grp][l32];
+      const uint4 *src = &p_lds[ps][grp][lane];
+      uint4 pw4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pw4[j] = src[64 * j];
+      bf16x8 vf[2][4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, voff, 0, db);
+      // Rows whose max did not rise have alpha exactly 1.
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int cur = bt & 1, nxt = cur ^ 1;
+        if (bt < 3) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, voff, bt + 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], __builtin_bit_cast(bf16x8, pw4[bt]), o[db], 0, 0, 0);
+      }
+    };
+    // Step 0 has no tile to apply yet.
+    dma(Vh, 1, v_lds[1], false);
+    dma(Kh, 3, k_lds[3], true);
+    end_step();
+    int vs = 0;   // V ring slot of tile kt - 1
+    for (int kt = 1; kt < n_steps; ++kt) {
+      const int vn = vs == kVSlots - 1 ? 0 : vs + 1;
+      const int vi = vn == kVSlots - 1 ? 0 : vn + 1;   // slot of tile kt + 1
+      dma(Vh, kt + 1, v_lds[vi], false);
+      dma(Kh, kt + 3, k_lds[(kt + 3) % kSlots], true);
+      apply((kt - 1) & 1, v_lds[vs]);
+      vs = vn;
+      end_step();
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    apply((n_steps - 1) & 1, v_lds[vs]);
+    const float *es = reinterpret_cast<const float *>(&p_lds[0][grp][0]);
+    store_row<kLse>(o, es[l32], es[32 + l32], head_off, head, qrow, Lq, g, O, O32, lse_out);
   }
 }
 
@@ -472,11 +705,11 @@ namespace {
 
 // Main launch + tail launch.  Units run in rounds of one 8-wave workgroup per
 // CU; when the last round would leave at least half the CUs idle (r <= CUs/2
-// units left over), those r units instead run as 2r 4-wave workgroups, one
-// per CU, after the full rounds (the same stream orders the two launches).
-// A 4-wave workgroup has one wave per SIMD to itself, so the tail round takes
-// well under a full round's time.  Which launch a unit lands in depends on H
-// and on the device, but a row's arithmetic does not.
+// units left over), those r units instead run as 2r attn_tail_kernel
+// workgroups of 128 rows, one per CU, after the full rounds (the same stream
+// orders the two launches).  The tail round then keeps every SIMD busy with
+// half a round's work.  Which launch a unit lands in depends on H and on the
+// device, but a row's arithmetic does not.
 template <bool kLse>
 hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, float *out32,
                         float *lse, int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
@@ -491,12 +724,12 @@ hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const int main_units = units - tail;
   const float sl2e = scale * kLog2e;
   if (main_units > 0) {
-    hipLaunchKernelGGL((attn_fwd_kernel<8, kLse>), dim3(main_units), dim3(512), 0, stream, q, k, v, out, out32,
+    hipLaunchKernelGGL((attn_fwd_kernel<kLse>), dim3(main_units), dim3(512), 0, stream, q, k, v, out, out32,
                        lse, Lq, Lk, kv_stride, n_qtiles, 0, sl2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (tail > 0) {
-    hipLaunchKernelGGL((attn_fwd_kernel<4, kLse>), dim3(2 * tail), dim3(256), 0, stream, q, k, v, out, out32,
+    hipLaunchKernelGGL((attn_tail_kernel<kLse>), dim3(2 * tail), dim3(512), 0, stream, q, k, v, out, out32,
                        lse, Lq, Lk, kv_stride, n_qtiles, main_units, sl2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -95,11 +95,11 @@ def test_attention_special_cases(gpu_lib):
 
 @pytest.mark.parametrize("L", [4900, 5000])
 def test_attention_tail_workgroups_bit_identical(gpu_lib, L):
-    """Ten heads in one launch (200 units of 256 rows: with 256 CUs all run as
-    8-wave workgroups) against one launch per head (20 units: all run as the
-    4-wave half-unit workgroups of the tail launch, the second half of the
-    last unit empty at L = 4900): every head bit-identical, and the full
-    launch within the bar of the oracle on sampled rows."""
+    """Ten heads in one launch (200 units of 256 rows: with 256 CUs all run in
+    the main launch) against one launch per head (20 units: all run as the
+    128-row producer/consumer workgroups of the tail launch, the second half
+    of the last unit empty at L = 4900): every head bit-identical, and the
+    full launch within the bar of the oracle on sampled rows."""
     import torch
     q, k, v = _raw(10, L, seed=40 + L)
     w = I.custom_workload(H=10, L=L)
