@@ -36,6 +36,8 @@ ATTN_SOURCE = os.path.join(ROOT, "exact_head_attention_amd", "csrc", "attn_fwd.h
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
 SQ_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_sq_counters.txt")
 PEAK_CLOCK_GHZ = 2.4                # the clock the published MFMA peaks assume
+SHADER_ENGINES = 32                 # MI355X: 8 XCDs x 4 shader engines
+SIMDS = 1024                        # 256 CUs x 4 SIMDs
 
 
 def source_digest(path=ATTN_SOURCE):
@@ -148,7 +150,56 @@ def summarize(args):
         for cname, short in (("FETCH_SIZE", "fetch_kib"), ("WRITE_SIZE", "write_kib")):
             tot = sum(sum(v) / len(v) for (key, c), v in per.items() if key.startswith("attn_") and c == cname)
             out.append(f"attn_{short}: {tot:.1f}")
+    if args.sq:
+        out += _sq_summary(args)
     print("\n".join(out))
+
+
+def _sq_summary(args):
+    """SQ counter passes (one directory each) over the attention's two
+    launches: utilisation ratios per launch and the shader clock of the
+    full-round launch (SQ_BUSY_CYCLES per shader engine over its duration)."""
+    kernels = (("main", "attn_fwd_kernel<false>"), ("tail", "attn_tail_kernel<false>"))
+    vals, clocks = {}, []
+    for d in args.sq:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                for key, kname in kernels:
+                    if kname in r["Kernel_Name"]:
+                        vals.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                        if key == "main" and r["Counter_Name"] == "SQ_BUSY_CYCLES":
+                            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                            clocks.append(float(r["Counter_Value"]) / SHADER_ENGINES / dur / 1e9)
+    out = [f"# rocprofv3 --pmc, {len(args.sq)} passes of SQ counters, workload {args.workload}: "
+           "attn_fwd_kernel<false> (main: full rounds) and attn_tail_kernel<false> (tail)",
+           f"# commands: {args.command}",
+           f"# {os.path.basename(ATTN_SOURCE)} sha256[:16] = {source_digest()}",
+           f"# mean per dispatch (sums over the chip); {SHADER_ENGINES} shader engines, {SIMDS} SIMDs; "
+           "SQ_WAVE_CYCLES and the wait/active counters count 4-cycle units"]
+    for key, _ in kernels:
+        m = {c: sum(v) / len(v) for (k, c), v in vals.items() if k == key}
+        if not m:
+            continue
+        for c in sorted(m):
+            out.append(f"{key}.{c:32s} {m[c]:12.4g}")
+        try:
+            per_se = m["SQ_BUSY_CYCLES"] / SHADER_ENGINES
+            busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS
+            out.append(f"# {key}: MFMA busy per SIMD {busy:.3g} of {per_se:.3g} cycles per SE = "
+                       f"{100 * busy / per_se:.1f}%")
+            for c in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
+                if c in m:
+                    out.append(f"# {key}: {c} / SQ_WAVE_CYCLES = {100 * m[c] / m['SQ_WAVE_CYCLES']:.1f}%")
+        except (KeyError, ZeroDivisionError):
+            pass
+    clocks.sort()
+    out.append("# shader clock per dispatch of the main launch = SQ_BUSY_CYCLES / shader engines / "
+               "(End_Timestamp - Start_Timestamp): " + ", ".join(f"{c:.3f}" for c in clocks) + " GHz")
+    out.append(f"workload: {args.workload}")
+    out.append(f"attn_source_sha256: {source_digest()}")
+    if clocks:
+        out.append(f"sclk_ghz: {clocks[len(clocks) // 2]:.3f}")
+    return out
 
 
 def log(msg):
@@ -346,6 +397,7 @@ def main():
                     help="format rocprofv3 CSV output (--kernel-stats DIR, --pmc DIR...) and exit")
     ap.add_argument("--kernel-stats", default=None)
     ap.add_argument("--pmc", nargs="*", default=None)
+    ap.add_argument("--sq", nargs="*", default=None, help="rocprofv3 --pmc directories of SQ counter passes")
     ap.add_argument("--command", default="")
     ap.add_argument("--source", default=None, help="kernel source whose hash the summary records")
     ap.add_argument("--parts", type=int, default=0,
