@@ -124,6 +124,7 @@ def summarize(args):
         if call_us > 0:
             out.append(f"# one h3_attention call = attn_fwd_kernel<false> (full rounds) + "
                        f"attn_tail_kernel<false> (tail, when launched): {call_us:.2f} us per call")
+        out += _prologue_split(args.kernel_stats)
     if args.pmc:
         per = {}
         for d in args.pmc:
@@ -153,6 +154,29 @@ def summarize(args):
     if args.sq:
         out += _sq_summary(args)
     print("\n".join(out))
+
+
+def _prologue_split(trace_dir):
+    """Per-dispatch prologue durations from the kernel trace, split into the
+    cold launches (each right after the read-only cache flush) and the
+    in-step ones."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return []
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+    cold, warm, prev = [], [], ""
+    for r in rows:
+        if "qknorm_rope_kernel" in r["Kernel_Name"]:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            (cold if "reduce_kernel" in prev else warm).append(d)
+        prev = r["Kernel_Name"]
+    out = []
+    for label, v in (("cold (after the cache flush)", cold), ("in step", warm)):
+        if v:
+            v.sort()
+            out.append(f"# qknorm_rope_kernel {label}: {len(v)} dispatches, median {v[len(v) // 2]:.2f} us, "
+                       f"min {v[0]:.2f}, max {v[-1]:.2f}")
+    return out
 
 
 def _sq_summary(args):
