@@ -69,7 +69,7 @@ def _prologue_check(gpu_lib, x, label):
         assert rel.max() <= 4e-3
 
 
-@pytest.mark.parametrize("name", ["tiny", "ws8"])
+@pytest.mark.parametrize("name", ["tiny", "ws8", "odd37726"])
 def test_prologue_parity(gpu_lib, name):
     _prologue_check(gpu_lib, host_inputs(name), name)
 
@@ -79,7 +79,9 @@ def test_prologue_parity_canvas_x3(gpu_lib):
     _prologue_check(gpu_lib, host_inputs("canvas128k"), "canvas128k")
 
 
-@pytest.mark.parametrize("L", [1, 5, 17, 300])
+@pytest.mark.parametrize("L", [1, 5, 17, 300, 32768 + 45])
 def test_prologue_ragged_lengths(gpu_lib, L):
+    """Lengths that end inside a 16-token workgroup, and (32768 + 45) one
+    that ends 45 tokens into a second 32768-token chunk."""
     w = I.custom_workload(H=3, L=L, n_audio=L // 3)
     _prologue_check(gpu_lib, I.make_inputs(w, seed=L), f"L={L}")
