@@ -751,30 +751,52 @@ hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint
 
 // Merge of P partial results: one 32-lane half-wave per (head, row); lane
 // holds 4 of the 128 columns.  lse = m + log(sum_p exp(lse_p - m)), out =
-// sum_p exp(lse_p - lse) * out_p, rounded once to bf16.
+// sum_p exp(lse_p - lse) * out_p, rounded once to bf16.  The partial rows are
+// read once, bypassing the caches.  kP > 0 fixes P at compile time: every
+// part's values are then loaded before any is used, so a thread's loads are
+// in flight together (P = 2 at H = 7, L = 32768: 50 us instead of 65 us).
+// kP = 0 takes P at run time.  Both forms add in the same order.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int kP>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ outs,
                                                          const float *__restrict__ lses, int P, long long rows,
                                                          uint16_t *__restrict__ out, float *__restrict__ lse_out) {
   const long long row = static_cast<long long>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int c = (threadIdx.x & 31) * 4;
   if (row >= rows) return;
+  auto part_lse = [&](int p) { return lses[p * rows + row]; };
+  auto part_row = [&](int p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(outs + (p * rows + row) * D + c));
+  };
   float m = -__builtin_inff();
-  for (int p = 0; p < P; ++p) m = __builtin_fmaxf(m, lses[p * rows + row]);
   float z = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = 0; p < P; ++p) {
-    const float w = (m == -__builtin_inff()) ? 0.f : __expf(lses[p * rows + row] - m);
-    const float4 x = *reinterpret_cast<const float4 *>(outs + (p * rows + row) * D + c);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float lp, const f32x4 &x) {
+    const float w = (m == -__builtin_inff()) ? 0.f : __expf(lp - m);
     z += w;
-    acc.x = __builtin_fmaf(w, x.x, acc.x);
-    acc.y = __builtin_fmaf(w, x.y, acc.y);
-    acc.z = __builtin_fmaf(w, x.z, acc.z);
-    acc.w = __builtin_fmaf(w, x.w, acc.w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, x[e], acc[e]);
+  };
+  if constexpr (kP > 0) {
+    float lv[kP];
+    f32x4 xv[kP];
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      lv[p] = part_lse(p);
+      xv[p] = part_row(p);
+    }
+#pragma unroll
+    for (int p = 0; p < kP; ++p) m = __builtin_fmaxf(m, lv[p]);
+#pragma unroll
+    for (int p = 0; p < kP; ++p) add(lv[p], xv[p]);
+  } else {
+    for (int p = 0; p < P; ++p) m = __builtin_fmaxf(m, part_lse(p));
+    for (int p = 0; p < P; ++p) add(part_lse(p), part_row(p));
   }
   const float inv = 1.0f / z;
   uint2 wv;
-  wv.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-  wv.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<uint2 *>(out + row * D + c) = wv;
   if (lse_out != nullptr && c == 0) lse_out[row] = m + __logf(z);
 }
@@ -782,9 +804,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
 hipError_t launch_attention_merge(const float *outs, const float *lses, int P, uint16_t *out, float *lse_out,
                                   int H, int L, hipStream_t stream) {
   const long long rows = static_cast<long long>(H) * L;
-  const long long blocks = (rows + 7) / 8;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, outs, lses, P,
-                     rows, out, lse_out);
+  const dim3 grid(static_cast<unsigned>((rows + 7) / 8)), block(256);
+  switch (P) {
+    case 1: hipLaunchKernelGGL(attn_merge_kernel<1>, grid, block, 0, stream, outs, lses, P, rows, out, lse_out); break;
+    case 2: hipLaunchKernelGGL(attn_merge_kernel<2>, grid, block, 0, stream, outs, lses, P, rows, out, lse_out); break;
+    case 3: hipLaunchKernelGGL(attn_merge_kernel<3>, grid, block, 0, stream, outs, lses, P, rows, out, lse_out); break;
+    case 4: hipLaunchKernelGGL(attn_merge_kernel<4>, grid, block, 0, stream, outs, lses, P, rows, out, lse_out); break;
+    default: hipLaunchKernelGGL(attn_merge_kernel<0>, grid, block, 0, stream, outs, lses, P, rows, out, lse_out);
+  }
   return hipGetLastError();
 }
 

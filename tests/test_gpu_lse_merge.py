@@ -49,10 +49,12 @@ def test_attention_lse_range_vs_oracle(gpu_lib, Lq, j0, j1):
         assert err.max() <= ATTN_TOL and lerr.max() <= LSE_TOL
 
 
-@pytest.mark.parametrize("cuts", [[0, 500, 1000], [0, 1, 333, 334, 1000], [0, 64, 128, 1000]])
+@pytest.mark.parametrize("cuts", [[0, 500, 1000], [0, 1, 333, 334, 1000], [0, 64, 128, 1000],
+                                  [0, 100, 200, 300, 400, 700, 1000]])
 def test_split_merge_equals_full(gpu_lib, cuts):
     """Keys split into uneven ranges, partials merged on the GPU: the bf16
-    output and merged lse match the oracle's unsplit attention."""
+    output and merged lse match the oracle's unsplit attention.  2, 3 and 4
+    parts take the merge's unrolled forms, 6 parts its run-time loop."""
     import torch
     q, k, v = _raw(3, 1000, seed=40, mult=2.0)
     s = 1 / math.sqrt(128)
