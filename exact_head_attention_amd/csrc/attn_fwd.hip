@@ -474,19 +474,21 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
 
 // Tail form: one 8-wave workgroup per 128 query rows (four 32-row groups).
 // Wave w < 4, the producer of group w, computes the scores, the running max
-// and sum and the bf16 weights P.  Wave w + 4, its consumer (placed on the
-// same SIMD), holds O and applies each tile's rescale and P.V one step
-// later, fed through LDS with P and the per-row factor alpha.  Every row
-// sees the same operations in the same order as in attn_fwd_kernel (an O
-// rescale by exactly 1 is an identity), so its bits do not change; the split
-// only gives each SIMD two waves where 128-row units would leave it one.
+// and the bf16 weights P.  Wave w + 4, its consumer (placed on the same
+// SIMD), holds O and the row sums: one step later it applies each tile's
+// rescale, sums the tile's weights and runs P.V, fed through LDS with P and
+// the per-row factor alpha.  Every row sees the same operations in the same
+// order as in attn_fwd_kernel (a rescale by exactly 1 is an identity), so
+// its bits do not change; the split only gives each SIMD two waves where
+// 128-row units would leave it one.  The producer's step is the longer one,
+// so the consumers also issue all tile loads.
 //   Step kt: producers score tile kt+1 and weigh tile kt; consumers apply
-//   tile kt-1.  Every wave issues its share of V tile kt+1 (3-slot ring, read
-//   in step kt+2) and K tile kt+3 (4-slot ring, read in step kt+2), and waits
-//   for all its older loads before the step's barrier.  Every LDS access of a
-//   step has completed before that barrier (lgkmcnt(0)), so a slot may be
-//   rewritten from the step after its last read on.  K + V + P rings:
-//   64 + 48 + 32 KB.
+//   tile kt-1 and load V tile kt+1 (3-slot ring, read in step kt+2) and K
+//   tile kt+3 (4-slot ring, read in step kt+2), four 1-KB pieces each per
+//   tensor, waiting for all their older loads before the step's barrier.
+//   Every LDS access of a step has completed before that barrier
+//   (lgkmcnt(0)), so a slot may be rewritten from the step after its last
+//   read on.  K + V + P rings: 64 + 48 + 32 KB.
 template <bool kLse>
 __global__ __launch_bounds__(512) void attn_tail_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -515,25 +517,42 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
   const int qrow = row0 + grp * 32 + l32;
 
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Only the consumers (waves 4-7) load tiles: four 1-KB pieces each.
   auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    dma_tile(base, t, Lk, dst, is_k, wave, wave_u, lane);
+    const int keys_left = Lk - t * kBc;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * (D * 2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = (wave - 4) + 4 * j;
+      const int row = 4 * n + (lane >> 4);
+      const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
+      const uint32_t m0 = lds_addr(dst) + ((wave_u - 4u) + 4u * j) * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0), "v"(row * (D * 2) + 16 * chunk), "s"(rs)
+                   : "memory");
+    }
   };
   auto end_step = [&]() {
-    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");   // all but this step's 4 loads
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");   // all but this step's 8 loads
     asm volatile("s_barrier" ::: "memory");
   };
 
   const int n_kt = (Lk + kBc - 1) / kBc;
   const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;   // as in attn_fwd_kernel
-  dma(Kh, 0, k_lds[0], true);
-  dma(Kh, 1, k_lds[1], true);
-  dma(Kh, 2, k_lds[2], true);
-  dma(Vh, 0, v_lds[0], false);
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // K tiles 0 and 1 (this wave's share)
+  if (wave_u >= 4) {
+    dma(Kh, 0, k_lds[0], true);
+    dma(Kh, 1, k_lds[1], true);
+    dma(Kh, 2, k_lds[2], true);
+    dma(Vh, 0, v_lds[0], false);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // K tiles 0 and 1
+  }
   __syncthreads();
 
   if (wave_u < 4) {
-    // Producer: the first half of attn_fwd_kernel's step, P and alpha to LDS.
+    // Producer: scores, running max and weights of attn_fwd_kernel's step; P
+    // and alpha to LDS.
     bf16x8 qf[8];
     {
       const int rows_left = Lq - row0 < 128 ? Lq - row0 : 128;
@@ -545,7 +564,6 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
     int koff[8];
     k_offsets(lane, koff);
     float m_run = -__builtin_inff();
-    float l_run0 = 0.f, l_run1 = 0.f;
     f32x16 s_a[2], s_b[2];
     s_a[0] = f32x16{};
     s_a[1] = f32x16{};
@@ -556,8 +574,6 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
     }
     mask_tile(s_a, 0, Lk, g);
     float mx = lane_half_max(max32(s_a[0], s_a[1])) * scale_log2e;
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    int vs = 1;   // V ring slot of tile kt + 1
 
     auto pstep = [&](auto r_c, auto mask_c, int kt, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
       constexpr int R = decltype(r_c)::value;
@@ -570,14 +586,9 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
         const float m_new = __builtin_fmaxf(m_run, mx);
         alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
-        l_run0 *= alpha;
-        l_run1 *= alpha;
       }
       if (g == 0) a_lds[R & 1][grp][l32] = alpha;
       const float neg_m = -m_run;
-      dma(Vh, kt + 1, v_lds[vs], false);
-      dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
-      vs = vs == kVSlots - 1 ? 0 : vs + 1;
       uint32_t pw[16];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -593,17 +604,13 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i], scale_log2e, neg_m));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[b][i + 1], scale_log2e, neg_m));
           pw[2 * c + e] = pack_bf16x2(p0, p1);
-          if (e == 0)
-            l_run0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run0, false);
-          else
-            l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[2 * c + e]), ones, l_run1, false);
         }
         s_nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][1], qf[c], c == 0 ? f32x16{} : s_nxt[1], 0, 0, 0);
         if (c < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's K reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);              // VALU/TRANS
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
+        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);              // VALU/TRANS
       }
       // pw[4j .. 4j+3] feeds the consumer's k-step j: lane-major 16-byte pieces.
       uint4 *pd = &p_lds[R & 1][grp][lane];
@@ -628,23 +635,22 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
       pstep(std::integral_constant<int, 2>{}, masked, kt + 2, s_a, s_b);
       pstep(std::integral_constant<int, 3>{}, masked, kt + 3, s_b, s_a);
     }
-    // The row's total and max for the consumer, in P slot 0 (n_steps is even,
-    // so slot 0 was last read in step n_steps - 1).
-    const float l_tot = lane_half_sum(l_run0 + l_run1);
+    // The row's max for the consumer, in P slot 0 (n_steps is even, so slot
+    // 0 was last read in step n_steps - 1).
     float *ed = reinterpret_cast<float *>(&p_lds[0][grp][0]);
-    if (g == 0) {
-      ed[l32] = l_tot;
-      ed[32 + l32] = m_run;
-    }
+    if (g == 0) ed[32 + l32] = m_run;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
   } else {
-    // Consumer: O = O * alpha + P.V, one tile behind its producer.
+    // Consumer: l = l * alpha + sum(P), O = O * alpha + P.V, one tile behind
+    // its producer; all tile loads.
     f32x16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     int voff[4];
     v_offsets(lane, voff);
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float l_run0 = 0.f, l_run1 = 0.f;
     auto apply = [&](int ps, const uint16_t *vp) {
       const float alpha = a_lds[ps][grp][l32];
       const uint4 *src = &p_lds[ps][grp][lane];
@@ -656,10 +662,19 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
       for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, voff, 0, db);
       // Rows whose max did not rise have alpha exactly 1.
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        l_run0 *= alpha;
+        l_run1 *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      const uint32_t pw[16] = {pw4[0].x, pw4[0].y, pw4[0].z, pw4[0].w, pw4[1].x, pw4[1].y, pw4[1].z, pw4[1].w,
+                               pw4[2].x, pw4[2].y, pw4[2].z, pw4[2].w, pw4[3].x, pw4[3].y, pw4[3].z, pw4[3].w};
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        l_run0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, l_run0, false);
+        l_run1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i + 1]), ones, l_run1, false);
       }
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
@@ -691,7 +706,7 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
     asm volatile("s_barrier" ::: "memory");
     apply((n_steps - 1) & 1, v_lds[vs]);
     const float *es = reinterpret_cast<const float *>(&p_lds[0][grp][0]);
-    store_row<kLse>(o, es[l32], es[32 + l32], head_off, head, qrow, Lq, g, O, O32, lse_out);
+    store_row<kLse>(o, lane_half_sum(l_run0 + l_run1), es[32 + l32], head_off, head, qrow, Lq, g, O, O32, lse_out);
   }
 }
 
