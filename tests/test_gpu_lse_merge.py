@@ -74,6 +74,23 @@ def test_split_merge_equals_full(gpu_lib, cuts):
     assert worst <= ATTN_TOL
 
 
+def test_attention_lse_tail_workgroups_bit_identical(gpu_lib):
+    """The partial form through both kernels: ten heads in one launch (200
+    units: all in the main launch) against one launch per head (20 units: all
+    in the producer/consumer tail launch), over a key range given as a pointer
+    offset.  out and lse bit-identical per head."""
+    import torch
+    q, k, v = _raw(10, 4900, seed=44)
+    a, b = 100, 4037
+    out_all, lse_all = gpu_lib.attention_lse(q, k[:, a:b], v[:, a:b])
+    for h in range(10):
+        out_h, lse_h = gpu_lib.attention_lse(q[h:h + 1], k[h:h + 1, a:b], v[h:h + 1, a:b])
+        torch.cuda.synchronize()
+        assert torch.equal(out_all[h], out_h[0]), f"head {h}: out differs between the launches"
+        assert torch.equal(lse_all[h], lse_h[0]), f"head {h}: lse differs between the launches"
+    assert bool(torch.isfinite(out_all).all()) and bool(torch.isfinite(lse_all).all())
+
+
 def test_merge_single_part_is_rounding_of_it(gpu_lib):
     """Special case: merging one part returns its bf16 rounding (RNE) exactly."""
     import torch
