@@ -163,7 +163,7 @@ static int check_qkv_proj(const void *x, const void *wq, const void *wk, const v
                           int hidden, int D, float eps) {
   if (!x || !wq || !wk || !wv || !gamma_q || !gamma_k || !cos || !sin || !q || !k || !v) return H3_ERR_NULL;
   if (fp8 && (!x_scale || !w_scale)) return H3_ERR_NULL;
-  const int step = fp8 ? 64 : 32;   // hidden elements per 64-byte step
+  const int step = fp8 ? 64 : 32;   // hidden elements per 64 bytes: half of the kernel's 128-byte step
   if (!shape_ok(H, L) || hidden < step || hidden % step != 0 || hidden > (1 << 20) ||
       h3::qkv_proj_grid(H, L) >= (int64_t{1} << 31))
     return H3_ERR_SHAPE;

@@ -24,14 +24,16 @@
 //     column and 16 features per lane, so a token's sum of squares over its
 //     128 features is lane-local plus one lane-half exchange, and each RoPE
 //     pair (2j, 2j+1) sits in one lane.
-//   * The hidden dimension streams in steps of 64 bytes per row (32 bf16 or
-//     64 fp8 elements) through a 4-slot LDS ring: buffer loads with the
+//   * The hidden dimension streams in steps of 128 bytes per row (64 bf16 or
+//     128 fp8 elements) through a 2-slot LDS ring: buffer loads with the
 //     LDS-destination bit put each step's weight rows and 256 token rows in
-//     LDS three steps ahead, with no register staging.  Rows are 64 bytes
-//     with their four 16-byte chunks swizzled by (row / 4) % 4, so the 16
-//     rows of a fragment read hit 16 distinct bank groups.  The descriptor
-//     ranges make the last partial token tile (and an odd 3H's empty head
-//     slot) read zeros, and nothing is written past L.
+//     LDS one step ahead, with no register staging.  Rows are 128 bytes with
+//     their eight 16-byte chunks swizzled by (row / 2) % 8, so the 16 rows of
+//     a fragment read hit 16 distinct bank groups.  A hidden size that ends
+//     halfway through a step loads zeros into the last step's second half,
+//     whose products then add exact zeros.
+//     The descriptor ranges make the last partial token tile (and an odd 3H's
+//     empty head slot) read zeros, and nothing is written past L.
 //   * fp8 form: OCP e4m3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
 //     block scales), each lane's fragment 32 consecutive hidden elements of
 //     its row for both operands; any fixed split of a step's elements over
@@ -70,9 +72,11 @@ template <bool kFp8> constexpr int slots_of() { return kFp8 ? 2 : 3; }
 template <bool kFp8> constexpr int threads_of() { return 64 * ranges_of<kFp8>() * slots_of<kFp8>(); }
 constexpr int kGroupTiles = 8;       // token tiles per placement group
 constexpr int kBufferFlags = 0x00020000;
-constexpr int kStepBytes = 64;       // bytes of each row per step (32 bf16 or 64 fp8 hidden elements)
+constexpr int kStepBytes = 128;      // bytes of each row per step (64 bf16 or 128 fp8 hidden elements)
 constexpr int kRowElems = kStepBytes / 2;   // uint16 per LDS row (no padding)
-constexpr int kRing = 4;             // LDS ring depth (steps) for each of W and X
+constexpr int kChunks = kStepBytes / 16;    // 16-byte chunks per row
+constexpr int kPieceRows = 1024 / kStepBytes;   // rows per 1-KB load
+constexpr int kRing = 2;             // LDS ring depth (steps) for each of W and X
 constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -87,10 +91,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)(p)));
 }
 
-// Chunk swizzle inside a 64-byte LDS row (4 chunks of 16 bytes): a fragment
-// read takes one logical chunk from 16 consecutive rows; rows 4 apart share
-// banks, and the swizzle puts those 4 rows in 4 different chunks.
-__device__ __forceinline__ int row_swz(int row) { return (row >> 2) & 3; }
+// Chunk swizzle inside a 128-byte LDS row (8 chunks of 16 bytes): a fragment
+// read takes one logical chunk from 16 consecutive rows; rows 2 apart share
+// banks, and the swizzle puts those 8 pairs of rows in 8 different chunks.
+__device__ __forceinline__ int row_swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
   constexpr int kTS = ts_of<kFp8>();
   constexpr int kWaves = threads_of<kFp8>() / 64;
   constexpr int kRows = kSlots * D;          // weight rows per workgroup
-  constexpr int kXLoads = kTok / 16;         // 1 KB loads per step for the token rows
+  constexpr int kWPieces = D / kPieceRows / 8;   // 1-KB loads per head slot and weight-loading wave
+  constexpr int kXLoads = kTok / kPieceRows;     // 1-KB loads per step for the token rows
   __shared__ __attribute__((aligned(1024))) uint16_t w_lds[kRing][kRows * kRowElems];
   __shared__ __attribute__((aligned(1024))) uint16_t x_lds[kRing][kTok * kRowElems];
 
@@ -157,65 +162,63 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
 
   // Steps go from global memory straight into LDS (buffer loads with the
   // LDS-destination bit), three steps ahead of the one being multiplied.
-  // Load j of wave w writes rows 16n .. 16n+15 (n = w + kWaves j) of the
-  // step's weight rows or 256 token rows as one contiguous kilobyte: lane
-  // i lands in row 16n + i/4 at physical chunk i%4 and fetches the row's
-  // logical chunk (i%4) ^ swizzle.  Rows past 3H or past L read as zeros
-  // (descriptor range).  The waits below are explicit.
+  // A load writes rows 8n .. 8n+7 of the step's weight rows or 256 token
+  // rows as one contiguous kilobyte: lane i lands in row 8n + i/8 at
+  // physical chunk i%8 and fetches the row's logical chunk (i%8) ^ swizzle.
+  // Rows past 3H or past L read as zeros (descriptor range), and so does the
+  // second half of a final half step (its lanes point past the range).  The
+  // waits below are explicit.
   // Each load sets m0 (its LDS destination) itself.  m0 cannot be named as
   // clobbered (the compiler reserves it); no compiler-generated instruction
   // in this kernel reads or writes it.
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int dma_row = lane >> 2;
+  const int dma_row = lane / kChunks;
   // Token-row loads: all waves with 8, waves 8.. with 12 or 16.
   constexpr int kXFirst = kWaves == 8 ? 0 : 8;
   constexpr int kXWaves = kWaves - kXFirst;
+  // Past every descriptor's range: a tile's descriptor covers at most 256 rows
+  // of 2^21 bytes (the API bounds hidden).
+  constexpr uint32_t kPastRange = 1u << 30;
   auto dma_step = [&](int ks, int slot) {
     const uint32_t kb = static_cast<uint32_t>(ks) * kStepBytes;
-    // Weight rows: waves 0..7 load 16-row block w of every head slot.
+    const bool half = row_bytes - ks * kStepBytes < kStepBytes;   // only the first half exists
+    auto off = [&](int row, int ch) {
+      return half && ch >= kChunks / 2 ? kPastRange : static_cast<uint32_t>(row * row_bytes) + kb + 16 * ch;
+    };
+    // Weight rows: waves 0..7 load 16-row block w of every head slot, as
+    // kWPieces loads of 8 rows each.
     if (wave_u < 8u) {
 #pragma unroll
-      for (int h = 0; h < kSlots; ++h) {
-        const int row = 16 * wave + dma_row;    // row within head slot h
-        const int ch = (lane & 3) ^ row_swz(row);
-        const uint32_t m0 = lds_addr(w_lds[slot]) + (8u * h + wave_u) * 1024u;
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :
-                     : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rw[h])
-                     : "memory");
-      }
+      for (int h = 0; h < kSlots; ++h)
+#pragma unroll
+        for (int pc = 0; pc < kWPieces; ++pc) {
+          const int row = kPieceRows * (kWPieces * wave + pc) + dma_row;   // row within head slot h
+          const int ch = (lane % kChunks) ^ row_swz(row);
+          const uint32_t m0 = lds_addr(w_lds[slot]) + ((8u * h + wave_u) * kWPieces + pc) * 1024u;
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :
+                       : "s"(m0), "v"(off(row, ch)), "s"(rw[h])
+                       : "memory");
+        }
     }
-    // Token rows: 16 blocks of 16, two per wave with 8 waves, or four per
-    // wave for waves 8..11 with 12.
+    // Token rows: 32 blocks of 8, four per wave with 8 waves, eight per
+    // wave for waves 8..11 with 12, four for waves 8..15 with 16.
     if (wave_u >= static_cast<uint32_t>(kXFirst)) {
 #pragma unroll
       for (int j = 0; j < kXLoads / kXWaves; ++j) {
         const uint32_t nu = wave_u - kXFirst + kXWaves * j;
-        const int row = 16 * (wave - kXFirst + kXWaves * j) + dma_row;
-        const int ch = (lane & 3) ^ row_swz(row);
+        const int row = kPieceRows * (wave - kXFirst + kXWaves * j) + dma_row;
+        const int ch = (lane % kChunks) ^ row_swz(row);
         const uint32_t m0 = lds_addr(x_lds[slot]) + nu * 1024u;
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :
-                     : "s"(m0), "v"(row * row_bytes + kb + 16 * ch), "s"(rx)
+                     : "s"(m0), "v"(off(row, ch)), "s"(rx)
                      : "memory");
       }
     }
   };
-  // This wave's loads per step: kSlots of weight rows (waves 0..7) plus its
-  // token-row loads.
-  const int per_step = (wave_u < 8u ? kSlots : 0) + (wave_u >= static_cast<uint32_t>(kXFirst) ? kXLoads / kXWaves : 0);
   static_assert(kWaves == 8 || kWaves == 12 || kWaves == 16, "load split above");
-  auto dma_wait = [&](int ahead) {
-    if (ahead >= 2) {
-      // Two steps' loads may stay outstanding (3 or 4 per step and wave with
-      // 8 or 12 waves, 2 with 16).
-      if constexpr (kWaves == 16) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if (per_step == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-  };
+  static_assert(kXLoads % (kWaves == 8 ? 8 : kWaves - 8) == 0, "token loads split evenly");
 
   // Wave (sl, th): head slot sl of the tile, tokens 32 kTS th .. + 32 kTS - 1.
   const int sl = wave % kSlots, th = wave / kSlots;
@@ -225,21 +228,21 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
 #pragma unroll
     for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] = f32x16{};
 
-  const int n_k = row_bytes / kStepBytes;   // hidden is a multiple of the step (the API checks)
-#pragma unroll
-  for (int r = 0; r < kRing - 1; ++r)
-    if (r < n_k) dma_step(r, r);
-  dma_wait(n_k > 2 ? 2 : 0);   // step 0 is in LDS (this wave's share)
+  // hidden is a multiple of half a step (the API checks); a final half step
+  // runs as a whole one over zeros.
+  const int n_k = (row_bytes + kStepBytes - 1) / kStepBytes;
+  dma_step(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // step 0 is in LDS (this wave's share)
   __syncthreads();
 
   // Fragment addresses: A = weight row 128 sl + 32 fs + l32, B = token row
-  // 32 kTS th + 32 ts + l32, both with swizzle (l32 >> 2) & 3.  bf16: logical
-  // chunk 2kk + g; fp8: logical chunks 2g and 2g+1 (32 bytes).
+  // 32 kTS th + 32 ts + l32, both with swizzle (l32 >> 1) & 7.  bf16
+  // sub-step kk (16 elements): logical chunk 2kk + g; fp8 sub-step kk (64
+  // elements): logical chunks 4kk + 2g and 4kk + 2g + 1 (32 bytes).
   const int sw_l = row_swz(l32);
   const uint16_t *wa = &w_lds[0][(sl * D + l32) * kRowElems];
   const uint16_t *xb = &x_lds[0][(th * 32 * kTS + l32) * kRowElems];
-  const int c0 = 8 * ((kFp8 ? 2 * g : g) ^ sw_l);   // uint16 offset of the first chunk
-  const int c1 = 8 * ((kFp8 ? 2 * g + 1 : 2 + g) ^ sw_l);
+  auto chunk_off = [&](int c) { return 8 * (c ^ sw_l); };   // uint16 offset of logical chunk c
   auto frag32 = [](const uint16_t *p0, const uint16_t *p1) {
     const uint4 lo = *reinterpret_cast<const uint4 *>(p0);
     const uint4 hi = *reinterpret_cast<const uint4 *>(p1);
@@ -247,29 +250,34 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
                  static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
   };
   // Step ks multiplies slot ks % kRing (R, a compile-time value) after
-  // issuing step ks+3 into slot (ks+3) % kRing, which held step ks-1: every
-  // wave finished reading it before the barrier that ended step ks-1.
+  // issuing step ks+1 into the other slot, which held step ks-1: every wave
+  // finished reading it before the barrier that ended step ks-1.
   auto step = [&](auto r_c, int ks) {
     constexpr int R = decltype(r_c)::value;
-    if (ks + kRing - 1 < n_k) dma_step(ks + kRing - 1, (R + kRing - 1) % kRing);
+    constexpr int kSub = kFp8 ? kChunks / 4 : kChunks / 2;   // 64-element (fp8) or 16-element (bf16) sub-steps
+    if (ks + 1 < n_k) dma_step(ks + 1, (R + 1) % kRing);
     const uint16_t *wab = wa + R * (kRows * kRowElems);
     const uint16_t *xbb = xb + R * (kTok * kRowElems);
     if constexpr (kFp8) {
-      i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kRowElems + c0, wab + i * 32 * kRowElems + c1);
+      for (int kk = 0; kk < kSub; ++kk) {
+        const int ca = chunk_off(4 * kk + 2 * g), cb = chunk_off(4 * kk + 2 * g + 1);
+        i32x8 a[4], b[kTS];
 #pragma unroll
-      for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kRowElems + c0, xbb + i * 32 * kRowElems + c1);
+        for (int i = 0; i < 4; ++i) a[i] = frag32(wab + i * 32 * kRowElems + ca, wab + i * 32 * kRowElems + cb);
 #pragma unroll
-      for (int fs = 0; fs < 4; ++fs)
+        for (int i = 0; i < kTS; ++i) b[i] = frag32(xbb + i * 32 * kRowElems + ca, xbb + i * 32 * kRowElems + cb);
 #pragma unroll
-        for (int ts = 0; ts < kTS; ++ts)
-          acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
-                                                                        kE8M0One, 0, kE8M0One);
+        for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+          for (int ts = 0; ts < kTS; ++ts)
+            acc[fs][ts] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[fs], b[ts], acc[fs][ts], 0, 0, 0,
+                                                                          kE8M0One, 0, kE8M0One);
+      }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int cc = kk == 0 ? c0 : c1;
+      for (int kk = 0; kk < kSub; ++kk) {
+        const int cc = chunk_off(2 * kk + g);
         bf16x8 a[4], b[kTS];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(wab + i * 32 * kRowElems + cc);
@@ -282,15 +290,13 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
             acc[fs][ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fs], b[ts], acc[fs][ts], 0, 0, 0);
       }
     }
-    // Step ks+1 must be in LDS: it was issued two steps before the newest.
-    dma_wait(n_k - 1 - ks > 2 ? 2 : 0);
+    // Step ks+1 must be in LDS before the barrier.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
   for (int ks = 0; ks < n_k; ks += kRing) {
     step(std::integral_constant<int, 0>{}, ks);
     if (ks + 1 < n_k) step(std::integral_constant<int, 1>{}, ks + 1);
-    if (ks + 2 < n_k) step(std::integral_constant<int, 2>{}, ks + 2);
-    if (ks + 3 < n_k) step(std::integral_constant<int, 3>{}, ks + 3);
   }
 
   // Epilogue.  acc[fs][ts][i] = feature 32fs + 8(i/4) + 4g + i%4 of the
