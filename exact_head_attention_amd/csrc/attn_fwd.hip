@@ -133,27 +133,29 @@ __device__ __forceinline__ float max32(const f32x16 &a, const f32x16 &b) {
 
 constexpr int kWaves = 8;   // waves per workgroup in both kernels
 
-// Wave `wave` (of 8) moves its two 1-KB pieces of 64-key tile t of one
-// tensor from global memory straight into LDS (buffer loads with the
-// LDS-destination bit).  Piece j covers rows 4n .. 4n+3, n = wave + 8j, as
-// one contiguous kilobyte: lane i lands in row 4n + i/16 at physical chunk
-// i%16, so it fetches the row's logical chunk (i%16) ^ swizzle.  Keys at or
-// past Lk read as zeros (the descriptor covers only the tile's valid rows).
-// The loads are tracked by the vector-memory counter only; callers wait
-// explicitly.  Each load sets m0 (its LDS destination) itself.  m0 cannot be
-// named as clobbered (the compiler reserves it); no compiler-generated
-// instruction in these kernels reads or writes it.
+// Loader `ld` of kLoaders waves moves its 16 / kLoaders 1-KB pieces of
+// 64-key tile t of one tensor from global memory straight into LDS (buffer
+// loads with the LDS-destination bit).  Piece j covers rows 4n .. 4n+3,
+// n = ld + kLoaders j, as one contiguous kilobyte: lane i lands in row
+// 4n + i/16 at physical chunk i%16, so it fetches the row's logical chunk
+// (i%16) ^ swizzle.  Keys at or past Lk read as zeros (the descriptor covers
+// only the tile's valid rows).  The loads are tracked by the vector-memory
+// counter only; callers wait explicitly.  Each load sets m0 (its LDS
+// destination) itself.  m0 cannot be named as clobbered (the compiler
+// reserves it); no compiler-generated instruction in these kernels reads or
+// writes it.  ld_u is ld as a wave-uniform (scalar) value.
+template <int kLoaders>
 __device__ __forceinline__ void dma_tile(const uint16_t *base, int t, int Lk, const uint16_t *dst, bool is_k,
-                                         int wave, uint32_t wave_u, int lane) {
+                                         int ld, uint32_t ld_u, int lane) {
   const int keys_left = Lk - t * kBc;
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * (D * 2));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = wave + kWaves * j;
+  for (int j = 0; j < 16 / kLoaders; ++j) {
+    const int n = ld + kLoaders * j;
     const int row = 4 * n + (lane >> 4);
     const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
-    const uint32_t m0 = lds_addr(dst) + (wave_u + kWaves * j) * 1024u;
+    const uint32_t m0 = lds_addr(dst) + (ld_u + kLoaders * j) * 1024u;
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0), "v"(row * (D * 2) + 16 * chunk), "s"(rs)
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
 
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    dma_tile(base, t, Lk, dst, is_k, wave, wave_u, lane);
+    dma_tile<kWaves>(base, t, Lk, dst, is_k, wave, wave_u, lane);
   };
   // Each step issues two loads of V and then two of K.  Waiting until at
   // most one step's loads are outstanding completes all older ones.
@@ -519,20 +521,7 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Only the consumers (waves 4-7) load tiles: four 1-KB pieces each.
   auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    const int keys_left = Lk - t * kBc;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(base + static_cast<size_t>(t) * kBc * D, (keys_left < kBc ? keys_left : kBc) * (D * 2));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = (wave - 4) + 4 * j;
-      const int row = 4 * n + (lane >> 4);
-      const int chunk = (lane & 15) ^ (is_k ? k_swz(row) : v_swz(row));
-      const uint32_t m0 = lds_addr(dst) + ((wave_u - 4u) + 4u * j) * 1024u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :
-                   : "s"(m0), "v"(row * (D * 2) + 16 * chunk), "s"(rs)
-                   : "memory");
-    }
+    dma_tile<4>(base, t, Lk, dst, is_k, wave - 4, wave_u - 4u, lane);
   };
   auto end_step = [&]() {
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");   // all but this step's 8 loads
