@@ -82,9 +82,6 @@ constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
 }
-__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 typedef __attribute__((address_space(3))) char lds_char;
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
