@@ -30,7 +30,7 @@ SOURCE_FLAGS = {
 # Packed-fp32 VALU forms are switched off for all device code.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-function",
+    "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
