@@ -113,6 +113,22 @@ def test_attention_tail_workgroups_bit_identical(gpu_lib, L):
         assert torch.equal(single[h], full[h]), f"head {h} differs between the launches"
 
 
+@pytest.mark.parametrize("H,L", [(1, 4096), (3, 1000)])
+def test_attention_tail_launch_repeat_bit_identical(gpu_lib, H, L):
+    """Race check of the tail launch's producer/consumer handoff through LDS:
+    shapes whose units all run in the tail kernel, launched 20 times back to
+    back, every output bit-identical to the first (a missed wait or barrier
+    would let some launch read a half-written slot)."""
+    import torch
+    q, k, v = _raw(H, L, seed=60 + L)
+    first = gpu_lib.attention(q, k, v)
+    outs = [gpu_lib.attention(q, k, v) for _ in range(20)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, first), f"launch {i + 1} differs from the first"
+    assert bool(torch.isfinite(first.float()).all())
+
+
 def test_attention_peaky_logits(gpu_lib):
     """Large logits (q, k ~ 3 N(0,1) at scale 1/sqrt(128): logit sd ~ 9) stress
     the running max and the rescaling of the accumulator."""
