@@ -33,6 +33,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E peak
 CALIB_COPY_BYTES = 512 << 20        # plain device copy whose counters calibrate FETCH/WRITE_SIZE
 ATTN_SOURCE = os.path.join(ROOT, "exact_head_attention_amd", "csrc", "attn_fwd.hip")
+PROLOGUE_SOURCE = os.path.join(ROOT, "exact_head_attention_amd", "csrc", "qknorm_rope.hip")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
 SQ_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_sq_counters.txt")
 PEAK_CLOCK_GHZ = 2.4                # the clock the published MFMA peaks assume
@@ -63,6 +64,22 @@ def read_counter_summary(workload):
         write_scale = CALIB_COPY_BYTES / (float(kv["copy_write_kib"]) * 1024)
         return (float(kv["attn_fetch_kib"]) * 1024 * fetch_scale
                 + float(kv["attn_write_kib"]) * 1024 * write_scale)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def read_prologue_traffic(workload):
+    """HBM bytes per prologue launch from the committed counter summary (its
+    own FETCH/WRITE lines, scaled like the attention's), or None when missing,
+    for another workload, or for another prologue source."""
+    try:
+        kv = _summary_kv(COUNTER_SUMMARY)
+        if kv.get("prologue_source_sha256") != source_digest(PROLOGUE_SOURCE) or kv.get("workload") != workload:
+            return None
+        fetch_scale = CALIB_COPY_BYTES / (float(kv["copy_fetch_kib"]) * 1024)
+        write_scale = CALIB_COPY_BYTES / (float(kv["copy_write_kib"]) * 1024)
+        return (float(kv["prologue_fetch_kib"]) * 1024 * fetch_scale
+                + float(kv["prologue_write_kib"]) * 1024 * write_scale)
     except (OSError, KeyError, ValueError):
         return None
 
@@ -132,6 +149,7 @@ def summarize(args):
                 for r in csv.DictReader(open(f)):
                     key = ("attn_main" if "attn_fwd_kernel<false>" in r["Kernel_Name"] else
                            "attn_tail" if "attn_tail_kernel<false>" in r["Kernel_Name"] else
+                           "prologue" if "qknorm_rope_kernel" in r["Kernel_Name"] else
                            "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
                         per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
@@ -141,6 +159,7 @@ def summarize(args):
                    f"{CALIB_COPY_BYTES} bytes each")
         out.append(f"workload: {args.workload}")
         out.append(f"attn_source_sha256: {source_digest()}")
+        out.append(f"prologue_source_sha256: {source_digest(PROLOGUE_SOURCE)}")
         for (key, cname), vals in sorted(per.items()):
             short = {"FETCH_SIZE": "fetch_kib", "WRITE_SIZE": "write_kib"}.get(cname, cname.lower())
             # The calibration copy is the largest copy dispatch (input uploads are small or use SDMA).
@@ -553,7 +572,8 @@ def main():
                      "achieved_GBps_cold": round(pbytes / (pro_cold_ms / 1e3) / 1e9, 1),
                      "peak_GBps": HBM_PEAK_GBS,
                      "frac_cold": round(pbytes / (pro_cold_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": pbytes},
+                     "bytes_per_launch": pbytes,
+                     "traffic": read_prologue_traffic(w.name)},
     }
     sclk = read_sclk_summary(w.name)
     if sclk is not None:
