@@ -127,7 +127,7 @@ def summarize(args):
         call_us = 0.0
         for r in rows:
             name = _kernel_short(r["Name"])
-            if name in ("attn_fwd_kernel<false>", "attn_tail_kernel<false>"):
+            if name in ("attn_fwd_kernel<false, false>", "attn_tail_kernel<false, false>"):
                 call_us += float(r["AverageNs"]) / 1e3
             if "reduce_kernel" in r["Name"]:
                 name = "torch amax (read-only cache flush)"
@@ -139,16 +139,16 @@ def summarize(args):
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
         if call_us > 0:
-            out.append(f"# one h3_attention call = attn_fwd_kernel<false> (full rounds) + "
-                       f"attn_tail_kernel<false> (tail, when launched): {call_us:.2f} us per call")
+            out.append(f"# one h3_attention call = attn_fwd_kernel<false, false> (full rounds) + "
+                       f"attn_tail_kernel<false, false> (tail, when launched): {call_us:.2f} us per call")
         out += _prologue_split(args.kernel_stats)
     if args.pmc:
         per = {}
         for d in args.pmc:
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
-                    key = ("attn_main" if "attn_fwd_kernel<false>" in r["Kernel_Name"] else
-                           "attn_tail" if "attn_tail_kernel<false>" in r["Kernel_Name"] else
+                    key = ("attn_main" if "attn_fwd_kernel<false, false>" in r["Kernel_Name"] else
+                           "attn_tail" if "attn_tail_kernel<false, false>" in r["Kernel_Name"] else
                            "prologue" if "qknorm_rope_kernel" in r["Kernel_Name"] else
                            "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
@@ -202,7 +202,7 @@ def _sq_summary(args):
     """SQ counter passes (one directory each) over the attention's two
     launches: utilisation ratios per launch and the shader clock of the
     full-round launch (SQ_BUSY_CYCLES per shader engine over its duration)."""
-    kernels = (("main", "attn_fwd_kernel<false>"), ("tail", "attn_tail_kernel<false>"))
+    kernels = (("main", "attn_fwd_kernel<false, false>"), ("tail", "attn_tail_kernel<false, false>"))
     vals, clocks = {}, []
     for d in args.sq:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -214,7 +214,7 @@ def _sq_summary(args):
                             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                             clocks.append(float(r["Counter_Value"]) / SHADER_ENGINES / dur / 1e9)
     out = [f"# rocprofv3 --pmc, {len(args.sq)} passes of SQ counters, workload {args.workload}: "
-           "attn_fwd_kernel<false> (main: full rounds) and attn_tail_kernel<false> (tail)",
+           "attn_fwd_kernel<false, false> (main: full rounds) and attn_tail_kernel<false, false> (tail)",
            f"# commands: {args.command}",
            f"# {os.path.basename(ATTN_SOURCE)} sha256[:16] = {source_digest()}",
            f"# mean per dispatch (sums over the chip); {SHADER_ENGINES} shader engines, {SIMDS} SIMDs; "
@@ -415,7 +415,7 @@ def bench_split_kv(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (ws8 inputs after the prologue)",
         "config": {"workload": f"ws8 attention with the keys cut at {cuts}: {P} h3_attention_lse launches + "
                                f"one h3_attention_merge", "H": w.H, "L": w.L, "D": w.D, "parts": P},
-        "roofline": {"kernel": "attn_fwd_kernel<true> (all parts)", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_kernel<true, false> (all parts)", "bound": "mfma",
                      "achieved": round(flops / (part_ms / 1e3) / 1e12, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (part_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_launch_ms": round(part_ms, 4)},
@@ -532,6 +532,27 @@ def main():
     del flush
     pro_cold_ms = float(np.median(pro_cold))
 
+    # The same attention with V given transposed (h3_attention_vt: the layout
+    # the projection's _vt forms write), timed launch by launch on the same
+    # stream; q and k are the step's last outputs.
+    l8 = (w.L + 7) // 8 * 8
+    vt = torch.zeros((w.H, w.D, l8), dtype=torch.bfloat16, device=dev)
+    vt[:, :, :w.L] = v.transpose(1, 2)
+    out_vt = torch.empty_like(q)
+    for _ in range(args.warmup):
+        B.attention_vt(q, k, vt, out=out_vt, scale=x["scale"])
+    vt_ms_all = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.attention_vt(q, k, vt, out=out_vt, scale=x["scale"])
+        b.record(stream)
+        vt_ms_all.append((a, b))
+    torch.cuda.synchronize()
+    vt_ms_all = [a.elapsed_time(b) for a, b in vt_ms_all]
+    vt_ms = float(np.mean(vt_ms_all))
+    del vt, out_vt
+
     # One plain 512 MiB device copy: the reference kernel whose HBM counters
     # calibrate FETCH_SIZE / WRITE_SIZE in counter runs of this script.
     src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -575,6 +596,12 @@ def main():
                      "bytes_per_launch": pbytes,
                      "traffic": read_prologue_traffic(w.name)},
     }
+    vt_tflops = flops / (vt_ms / 1e3) / 1e12
+    rec["attention_vt"] = {"call": "h3_attention_vt (V as [H][D][L]; the same bits as h3_attention)",
+                           "avg_launch_ms": round(vt_ms, 4), "min_launch_ms": round(min(vt_ms_all), 4),
+                           "achieved": round(vt_tflops, 2), "unit": "TFLOP/s",
+                           "frac": round(vt_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                           "speedup_vs_h3_attention": round(att_ms / vt_ms, 4)}
     sclk = read_sclk_summary(w.name)
     if sclk is not None:
         # The published peak assumes 2.4 GHz; the chip holds a lower clock

@@ -28,6 +28,8 @@ lib.h3_attention.restype = _i
 lib.h3_rope_tables.argtypes = [_vp, _i, _i, _d, _vp, _vp, _vp]
 lib.h3_rope_tables.restype = _i
 _ll = ctypes.c_longlong
+lib.h3_attention_vt.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp]
+lib.h3_attention_vt.restype = _i
 lib.h3_attention_lse.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _ll, _i, _f, _vp]
 lib.h3_attention_lse.restype = _i
 lib.h3_attention_merge.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp]
@@ -36,14 +38,19 @@ lib.h3_qkv_proj_qknorm_rope.argtypes = [_vp] * 11 + [_i, _i, _i, _i, _f, _vp]
 lib.h3_qkv_proj_qknorm_rope.restype = _i
 lib.h3_qkv_proj_fp8_qknorm_rope.argtypes = [_vp] * 13 + [_i, _i, _i, _i, _f, _vp]
 lib.h3_qkv_proj_fp8_qknorm_rope.restype = _i
+lib.h3_qkv_proj_qknorm_rope_vt.argtypes = [_vp] * 11 + [_i, _i, _i, _i, _i, _f, _vp]
+lib.h3_qkv_proj_qknorm_rope_vt.restype = _i
+lib.h3_qkv_proj_fp8_qknorm_rope_vt.argtypes = [_vp] * 13 + [_i, _i, _i, _i, _i, _f, _vp]
+lib.h3_qkv_proj_fp8_qknorm_rope_vt.restype = _i
 lib.h3_status_string.argtypes = [_i]
 lib.h3_status_string.restype = ctypes.c_char_p
 lib.h3_abi_version.argtypes = []
 lib.h3_abi_version.restype = _i
 
 HEAD_DIM = 128
-EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
-            "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope", "h3_status_string", "h3_abi_version")
+EXPORTED = ("h3_qknorm_rope", "h3_attention", "h3_attention_vt", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
+            "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope", "h3_qkv_proj_qknorm_rope_vt",
+            "h3_qkv_proj_fp8_qknorm_rope_vt", "h3_status_string", "h3_abi_version")
 
 
 class H3Error(RuntimeError):
@@ -126,6 +133,28 @@ def attention(q, k, v, out=None, scale: float | None = None):
     return out
 
 
+def attention_vt(q, k, vt, out=None, scale: float | None = None):
+    """attention() with V transposed: vt bf16 [H, 128, ldv], row (h, d) holding
+    v[h, :, d] in its first L columns (L <= ldv, ldv a multiple of 8; columns
+    L .. up to the next multiple of 8 finite).  Returns out bf16 [H, L, 128]."""
+    import torch
+    H, L, D = _hld(q, "q")
+    if tuple(k.shape) != (H, L, D):
+        raise ValueError("k must have q's shape")
+    if vt.dim() != 3 or vt.shape[0] != H or vt.shape[1] != D or vt.shape[2] < L:
+        raise ValueError(f"vt must be [{H}, {D}, ldv >= {L}], got {tuple(vt.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != (H, L, D):
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check("h3_attention_vt", lib.h3_attention_vt(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(vt, torch.bfloat16, "vt"),
+        _dev(out, torch.bfloat16, "out"), H, L, vt.shape[2], D, float(scale), _stream()))
+    return out
+
+
 def _kv_view(t, name):
     """Pointer and head stride of a key/value tensor [H, Lk, D] whose rows are
     contiguous (e.g. a key-range slice t_full[:, j0:j1] of a [H, L, D] tensor)."""
@@ -175,71 +204,78 @@ def attention_merge(outs, lses, out=None, want_lse: bool = False):
     return (out, lse_out) if want_lse else out
 
 
-def qkv_proj_qknorm_rope(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, eps: float = 1e-6, out=None):
+def _proj_shapes(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, out, ldv):
+    """Checks the projection's shapes; returns (H, L, C, out) with out
+    allocated when None (v as [H, 128, ldv] when ldv is not None)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError(f"x must be [L, hidden], got {tuple(x.shape)}")
+    L, C = x.shape
+    if wq.dim() != 2 or wq.shape[1] != C or wq.shape[0] % HEAD_DIM:
+        raise ValueError(f"wq must be [H*{HEAD_DIM}, {C}], got {tuple(wq.shape)}")
+    if tuple(wk.shape) != tuple(wq.shape) or tuple(wv.shape) != tuple(wq.shape):
+        raise ValueError("wq, wk and wv must have the same shape")
+    H = wq.shape[0] // HEAD_DIM
+    if tuple(cos.shape) != (L, HEAD_DIM // 2) or tuple(sin.shape) != (L, HEAD_DIM // 2):
+        raise ValueError(f"cos/sin must be [{L}, {HEAD_DIM // 2}]")
+    if gamma_q.numel() != HEAD_DIM or gamma_k.numel() != HEAD_DIM:
+        raise ValueError(f"gamma_q/gamma_k must have {HEAD_DIM} elements")
+    v_shape = (H, L, HEAD_DIM) if ldv is None else (H, HEAD_DIM, ldv)
+    if out is None:
+        out = tuple(torch.empty(s, dtype=torch.bfloat16, device=x.device)
+                    for s in ((H, L, HEAD_DIM), (H, L, HEAD_DIM), v_shape))
+    for t, n, s in zip(out, "qkv", ((H, L, HEAD_DIM), (H, L, HEAD_DIM), v_shape)):
+        if tuple(t.shape) != s:
+            raise ValueError(f"out {n} must be {list(s)}")
+    return H, L, C, out
+
+
+def qkv_proj_qknorm_rope(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, eps: float = 1e-6, out=None,
+                         ldv: int | None = None):
     """The rank's qkv projection with QK-RMSNorm + RoPE fused behind it.
 
     x: bf16 [L, hidden]; wq, wk, wv: bf16 [H*128, hidden] (a contiguous row
     slice of the full weight is fine); gamma fp32 [128]; cos, sin fp32
     [L, 64].  Returns (q, k, v), bf16 [H, L, 128] each (or fills `out`, a
-    (q, k, v) tuple of such tensors).
+    (q, k, v) tuple of such tensors).  With ldv (a multiple of 8, >= L), v is
+    written transposed as [H, 128, ldv] for attention_vt.
     """
     import torch
-    if x.dim() != 2:
-        raise ValueError(f"x must be [L, hidden], got {tuple(x.shape)}")
-    L, C = x.shape
-    if wq.dim() != 2 or wq.shape[1] != C or wq.shape[0] % HEAD_DIM:
-        raise ValueError(f"wq must be [H*{HEAD_DIM}, {C}], got {tuple(wq.shape)}")
-    if tuple(wk.shape) != tuple(wq.shape) or tuple(wv.shape) != tuple(wq.shape):
-        raise ValueError("wq, wk and wv must have the same shape")
-    H = wq.shape[0] // HEAD_DIM
-    if tuple(cos.shape) != (L, HEAD_DIM // 2) or tuple(sin.shape) != (L, HEAD_DIM // 2):
-        raise ValueError(f"cos/sin must be [{L}, {HEAD_DIM // 2}]")
-    if gamma_q.numel() != HEAD_DIM or gamma_k.numel() != HEAD_DIM:
-        raise ValueError(f"gamma_q/gamma_k must have {HEAD_DIM} elements")
-    if out is None:
-        out = tuple(torch.empty((H, L, HEAD_DIM), dtype=torch.bfloat16, device=x.device) for _ in range(3))
-    for t, n in zip(out, "qkv"):
-        if tuple(t.shape) != (H, L, HEAD_DIM):
-            raise ValueError(f"out {n} must be [{H}, {L}, {HEAD_DIM}]")
-    _check("h3_qkv_proj_qknorm_rope", lib.h3_qkv_proj_qknorm_rope(
-        _dev(x, torch.bfloat16, "x"), _dev(wq, torch.bfloat16, "wq"), _dev(wk, torch.bfloat16, "wk"),
-        _dev(wv, torch.bfloat16, "wv"), _dev(gamma_q, torch.float32, "gamma_q"),
-        _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
-        _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
-        _dev(out[2], torch.bfloat16, "v"), H, L, C, HEAD_DIM, float(eps), _stream()))
+    H, L, C, out = _proj_shapes(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, out, ldv)
+    args = [_dev(x, torch.bfloat16, "x"), _dev(wq, torch.bfloat16, "wq"), _dev(wk, torch.bfloat16, "wk"),
+            _dev(wv, torch.bfloat16, "wv"), _dev(gamma_q, torch.float32, "gamma_q"),
+            _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
+            _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
+            _dev(out[2], torch.bfloat16, "v")]
+    if ldv is None:
+        _check("h3_qkv_proj_qknorm_rope", lib.h3_qkv_proj_qknorm_rope(
+            *args, H, L, C, HEAD_DIM, float(eps), _stream()))
+    else:
+        _check("h3_qkv_proj_qknorm_rope_vt", lib.h3_qkv_proj_qknorm_rope_vt(
+            *args, H, L, int(ldv), C, HEAD_DIM, float(eps), _stream()))
     return out
 
 
 def qkv_proj_fp8_qknorm_rope(x, x_scale, wq, wk, wv, w_scale, gamma_q, gamma_k, cos, sin, eps: float = 1e-6,
-                             out=None):
+                             out=None, ldv: int | None = None):
     """The fp8 form: x float8_e4m3fn [L, hidden] with x_scale (fp32 tensor of
     one element), wq/wk/wv float8_e4m3fn [H*128, hidden] with the weight's
-    per-tensor w_scale.  Returns (q, k, v), bf16 [H, L, 128] each."""
+    per-tensor w_scale.  Returns (q, k, v), bf16 [H, L, 128] each (v as
+    [H, 128, ldv] when ldv is given)."""
     import torch
     f8 = torch.float8_e4m3fn
-    if x.dim() != 2:
-        raise ValueError(f"x must be [L, hidden], got {tuple(x.shape)}")
-    L, C = x.shape
-    if wq.dim() != 2 or wq.shape[1] != C or wq.shape[0] % HEAD_DIM:
-        raise ValueError(f"wq must be [H*{HEAD_DIM}, {C}], got {tuple(wq.shape)}")
-    if tuple(wk.shape) != tuple(wq.shape) or tuple(wv.shape) != tuple(wq.shape):
-        raise ValueError("wq, wk and wv must have the same shape")
     if x_scale.numel() != 1 or w_scale.numel() != 1:
         raise ValueError("x_scale and w_scale must hold one element each")
-    H = wq.shape[0] // HEAD_DIM
-    if tuple(cos.shape) != (L, HEAD_DIM // 2) or tuple(sin.shape) != (L, HEAD_DIM // 2):
-        raise ValueError(f"cos/sin must be [{L}, {HEAD_DIM // 2}]")
-    if gamma_q.numel() != HEAD_DIM or gamma_k.numel() != HEAD_DIM:
-        raise ValueError(f"gamma_q/gamma_k must have {HEAD_DIM} elements")
-    if out is None:
-        out = tuple(torch.empty((H, L, HEAD_DIM), dtype=torch.bfloat16, device=x.device) for _ in range(3))
-    for t, n in zip(out, "qkv"):
-        if tuple(t.shape) != (H, L, HEAD_DIM):
-            raise ValueError(f"out {n} must be [{H}, {L}, {HEAD_DIM}]")
-    _check("h3_qkv_proj_fp8_qknorm_rope", lib.h3_qkv_proj_fp8_qknorm_rope(
-        _dev(x, f8, "x"), _dev(x_scale, torch.float32, "x_scale"), _dev(wq, f8, "wq"), _dev(wk, f8, "wk"),
-        _dev(wv, f8, "wv"), _dev(w_scale, torch.float32, "w_scale"), _dev(gamma_q, torch.float32, "gamma_q"),
-        _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
-        _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
-        _dev(out[2], torch.bfloat16, "v"), H, L, C, HEAD_DIM, float(eps), _stream()))
+    H, L, C, out = _proj_shapes(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, out, ldv)
+    args = [_dev(x, f8, "x"), _dev(x_scale, torch.float32, "x_scale"), _dev(wq, f8, "wq"), _dev(wk, f8, "wk"),
+            _dev(wv, f8, "wv"), _dev(w_scale, torch.float32, "w_scale"), _dev(gamma_q, torch.float32, "gamma_q"),
+            _dev(gamma_k, torch.float32, "gamma_k"), _dev(cos, torch.float32, "cos"),
+            _dev(sin, torch.float32, "sin"), _dev(out[0], torch.bfloat16, "q"), _dev(out[1], torch.bfloat16, "k"),
+            _dev(out[2], torch.bfloat16, "v")]
+    if ldv is None:
+        _check("h3_qkv_proj_fp8_qknorm_rope", lib.h3_qkv_proj_fp8_qknorm_rope(
+            *args, H, L, C, HEAD_DIM, float(eps), _stream()))
+    else:
+        _check("h3_qkv_proj_fp8_qknorm_rope_vt", lib.h3_qkv_proj_fp8_qknorm_rope_vt(
+            *args, H, L, int(ldv), C, HEAD_DIM, float(eps), _stream()))
     return out

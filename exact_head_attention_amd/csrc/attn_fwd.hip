@@ -16,6 +16,9 @@
 //     LDS-destination bit), K three tiles and V two tiles ahead of their
 //     use, so no registers stage them and a load has two steps to land.  V
 //     is read as the transposed MFMA operand with ds_read_b64_tr_b16.
+//     h3_attention_vt takes V already transposed, [H][D][ldv] with keys
+//     contiguous: its tiles sit in LDS as [d][64 keys] and the same operand
+//     is a plain 16-byte read (half the LDS instructions for V).
 //   * Per wave and key tile, with v_mfma_f32_32x32x16_bf16:
 //       S^T (64 keys x 32 queries) = K_tile . Q^T        16 MFMAs, Q^T in VGPRs
 //       O^T (128 d  x 32 queries) += V_tile^T . P^T      16 MFMAs
@@ -91,6 +94,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 //      consecutive rows, which then sit in 4 disjoint groups of 4 chunks.
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+//   V^T tile [d][64 keys] (128-byte rows): (d / 2) % 8 -- a fragment read
+//      takes one logical chunk from 16 consecutive rows; rows 2 apart share
+//      banks, and the swizzle puts those 8 row pairs in 8 different chunks.
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
+// A V^T load offset past every descriptor's range (a head's V^T spans at
+// most 2^31 bytes): the load reads zeros.
+constexpr uint32_t kVtPastRange = 0xC0000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
@@ -163,6 +173,42 @@ __device__ __forceinline__ void dma_tile(const uint16_t *base, int t, int Lk, co
   }
 }
 
+// The V^T form of dma_tile: tile t of one head's V^T ([D][ldv], keys
+// contiguous) goes to LDS as [d][64 keys], 128 bytes per row.  Piece j
+// covers rows 8n .. 8n+7 (n = ld + kLoaders j) as one kilobyte: lane i lands
+// in row 8n + i/8 at physical chunk i%8 and fetches the row's logical chunk
+// (i%8) ^ vt_swz(row), keys t*64 + 8*logical .. +7.  With kMask, a chunk
+// whose first key is at or past Lk reads zeros (its offset lies past the
+// descriptor); the one chunk that straddles Lk reads the row's padding past
+// Lk, which only ever meets exact zero weights (the caller keeps it finite).
+// Callers pass kMask = false only for tiles that lie wholly below Lk: the
+// extra compare in every step's loads costs ~4% of the kernel's time
+// (it changes how the compiler interleaves the step).
+template <int kLoaders, bool kMask>
+__device__ __forceinline__ void dma_vt_tile(const uint16_t *base, int t, int Lk, int ldv, const uint16_t *dst, int ld,
+                                            uint32_t ld_u, int lane) {
+  // Row d of the tile starts d*ldv*2 bytes after base + t*64 keys; the range
+  // ends with the head (at most 2^31 bytes, so it is passed as raw bits).
+  const uint32_t range = static_cast<uint32_t>(D) * static_cast<uint32_t>(ldv) * 2u -
+                         static_cast<uint32_t>(t) * static_cast<uint32_t>(kBc * 2);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(base + static_cast<size_t>(t) * kBc), 0, static_cast<int>(range), kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < 16 / kLoaders; ++j) {
+    const int n = ld + kLoaders * j;
+    const int row = 8 * n + (lane >> 3);
+    const int chunk = (lane & 7) ^ vt_swz(row);
+    const uint32_t off = kMask && t * kBc + 8 * chunk >= Lk
+                             ? kVtPastRange
+                             : static_cast<uint32_t>(row) * static_cast<uint32_t>(ldv) * 2u + 16u * chunk;
+    const uint32_t m0 = lds_addr(dst) + (ld_u + kLoaders * j) * 1024u;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(rs)
+                 : "memory");
+  }
+}
+
 // K fragment of chunk pair c (A operand of the score product): row krow
 // (+32 for the second key block), logical chunk 2c + g, i.e. physical chunk
 // 2c ^ (g ^ (krow & 15)), krow = l32 with bits 2 and 3 swapped.
@@ -194,6 +240,12 @@ __device__ __forceinline__ bf16x8 vread(const uint16_t *vt, const int (&voff)[4]
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 4 * D));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The same fragment from a V^T tile: row d = 32db + l32, keys 16bt + 8g .. +7,
+// i.e. logical chunk 2bt + g of row d, one 16-byte read.
+__device__ __forceinline__ bf16x8 vread_t(const uint16_t *vt, int bt, int db, int l32, int g) {
+  const int d = 32 * db + l32;
+  return *reinterpret_cast<const bf16x8 *>(vt + d * kBc + 8 * ((2 * bt + g) ^ vt_swz(d)));
 }
 
 // Mask the keys of tile t at or past Lk (only the last, ragged tile has any).
@@ -248,14 +300,17 @@ __device__ __forceinline__ void store_row(const f32x16 (&o)[4], float l_tot, flo
 // natural log of sum_j exp(scale q.k_j) over the Lk keys given (the partial
 // form h3_attention_merge combines).  Queries: [H][Lq][D]; keys and values:
 // element (h, j, d) at h*kv_stride + j*D + d, j < Lk.
+// kVt = true (with kLse = false): V is transposed, element (h, j, d) at
+// (h*D + d)*ldv + j (h3_attention_vt); otherwise ldv is unused.
 //
 // One 8-wave workgroup per unit: block b covers unit unit_base + r, with r
 // the XCD-remapped b.
-template <bool kLse>
+template <bool kLse, bool kVt>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
-    long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
+    long long kv_stride, int ldv, int n_qtiles, int unit_base, float scale_log2e) {
+  static_assert(!(kLse && kVt), "the partial form takes V as [H][Lk][D]");
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kSlots][kTileElems];
 
@@ -271,7 +326,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Qh = Q + head_off;
   const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
-  const uint16_t *Vh = V + static_cast<size_t>(head) * kv_stride;
+  const uint16_t *Vh = V + static_cast<size_t>(head) * (kVt ? static_cast<long long>(D) * ldv : kv_stride);
   const int row_bytes = D * 2;
 
   // Q^T fragments (B operand): lane holds query row qrow, d = 16c + 8g .. +7.
@@ -288,9 +343,15 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   }
 
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    dma_tile<kWaves>(base, t, Lk, dst, is_k, wave, wave_u, lane);
+  // whole: tile t lies wholly below Lk (a compile-time fact at each call).
+  auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k, auto whole_c) {
+    if (kVt && !is_k)
+      dma_vt_tile<kWaves, !decltype(whole_c)::value>(base, t, Lk, ldv, dst, wave, wave_u, lane);
+    else
+      dma_tile<kWaves>(base, t, Lk, dst, is_k, wave, wave_u, lane);
   };
+  const std::integral_constant<bool, true> whole{};
+  const std::integral_constant<bool, false> ragged{};
   // Each step issues two loads of V and then two of K.  Waiting until at
   // most one step's loads are outstanding completes all older ones.
   auto dma_wait_all_but_one_pair = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
@@ -306,17 +367,25 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   // constant; the up to kSlots-1 extra tiles lie wholly past Lk, so their
   // weights are exactly 0 and their (zero-filled) V rows add exact zeros.
   const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;
-  dma(Vh, 0, v_lds[0], false);
-  dma(Kh, 0, k_lds[0], true);
-  dma(Kh, 1, k_lds[1], true);
-  dma(Vh, 1, v_lds[1], false);
-  dma(Kh, 2, k_lds[2], true);
+  dma(Vh, 0, v_lds[0], false, ragged);
+  dma(Kh, 0, k_lds[0], true, ragged);
+  dma(Kh, 1, k_lds[1], true, ragged);
+  dma(Vh, 1, v_lds[1], false, ragged);
+  dma(Kh, 2, k_lds[2], true, ragged);
   dma_wait_all_but_one_pair();   // K tiles 0, 1 and V tile 0 are in LDS (this wave's share)
   __syncthreads();
 
   int koff[8], voff[4];
   k_offsets(lane, koff);
   v_offsets(lane, voff);
+  // V fragment db of k-step bt, and the LDS reads one k-step's fragments take.
+  auto vfrag = [&](const uint16_t *vp, int bt, int db) {
+    if constexpr (kVt)
+      return vread_t(vp, bt, db, l32, g);
+    else
+      return vread(vp, voff, bt, db);
+  };
+  constexpr int kVReads = kVt ? 4 : 8;
 
   f32x16 s_a[2], s_b[2];
   {
@@ -378,8 +447,14 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     const float neg_m = -m_run;
 
     // (2) K fragments are read one MFMA pair ahead (ping-pong registers).
-    dma(Vh, kt + 2, v_lds[(R + 2) % kSlots], false);
-    dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true);
+    // Without the mask, V tile kt+2 is whole (see the loops below).
+    if constexpr (decltype(mask_c)::value) {
+      dma(Vh, kt + 2, v_lds[(R + 2) % kSlots], false, ragged);
+      dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true, ragged);
+    } else {
+      dma(Vh, kt + 2, v_lds[(R + 2) % kSlots], false, whole);
+      dma(Kh, kt + 3, k_lds[(R + 3) % kSlots], true, whole);
+    }
     uint32_t pw[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -389,7 +464,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
         ka[nxt][1] = kread(kp, koff, 1, c + 1);
       } else {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, voff, 0, db);
+        for (int db = 0; db < 4; ++db) vf[0][db] = vfrag(vp, 0, db);
       }
       s_nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cur][0], qf[c], c == 0 ? f32x16{} : s_nxt[0], 0, 0, 0);
 #pragma unroll
@@ -407,7 +482,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
       if (c < 7)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next pair's K reads
       else
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // P.V's first V reads
+        __builtin_amdgcn_sched_group_barrier(0x100, kVReads, 0);   // P.V's first V reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);              // VALU/TRANS
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
@@ -424,13 +499,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
       const int cur = bt & 1, nxt = cur ^ 1;
       if (bt < 3) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, voff, bt + 1, db);
+        for (int db = 0; db < 4; ++db) vf[nxt][db] = vfrag(vp, bt + 1, db);
       }
       const uint4 w = make_uint4(pw[4 * bt], pw[4 * bt + 1], pw[4 * bt + 2], pw[4 * bt + 3]);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], __builtin_bit_cast(bf16x8, w), o[db], 0, 0, 0);
-      if (bt < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // next k-step's V reads
+      if (bt < 3) __builtin_amdgcn_sched_group_barrier(0x100, kVReads, 0);   // next k-step's V reads
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
@@ -450,11 +525,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   // without the mask.  A data-dependent branch inside a step splits it into
   // basic blocks that the compiler schedules apart: it then sinks the
   // exponentials below the score products instead of interleaving them
-  // (measured: 3% for the full-round launch, 5% for the tail launch).
+  // (measured: 3% for the full-round launch, 5% for the tail launch).  With
+  // V^T the group's V loads (tiles kt+2 .. kt+5) must be whole as well.
   const std::integral_constant<bool, true> masked{};
   const std::integral_constant<bool, false> plain{};
+  constexpr int kWholeAhead = kVt ? 6 : 5;
   int kt = 0;
-  for (; (kt + 5) * kBc <= Lk; kt += kSlots) {
+  for (; (kt + kWholeAhead) * kBc <= Lk; kt += kSlots) {
     step(std::integral_constant<int, 0>{}, plain, kt, s_a, s_b);
     step(std::integral_constant<int, 1>{}, plain, kt + 1, s_b, s_a);
     step(std::integral_constant<int, 2>{}, plain, kt + 2, s_a, s_b);
@@ -491,11 +568,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
 //   Every LDS access of a step has completed before that barrier
 //   (lgkmcnt(0)), so a slot may be rewritten from the step after its last
 //   read on.  K + V + P rings: 64 + 48 + 32 KB.
-template <bool kLse>
+template <bool kLse, bool kVt>
 __global__ __launch_bounds__(512) void attn_tail_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
-    long long kv_stride, int n_qtiles, int unit_base, float scale_log2e) {
+    long long kv_stride, int ldv, int n_qtiles, int unit_base, float scale_log2e) {
+  static_assert(!(kLse && kVt), "the partial form takes V as [H][Lk][D]");
   constexpr int kVSlots = 3;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kVSlots][kTileElems];
@@ -515,13 +593,16 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
   if (row0 >= Lq) return;   // the empty half of a ragged last unit (uniform per block)
   const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
-  const uint16_t *Vh = V + static_cast<size_t>(head) * kv_stride;
+  const uint16_t *Vh = V + static_cast<size_t>(head) * (kVt ? static_cast<long long>(D) * ldv : kv_stride);
   const int qrow = row0 + grp * 32 + l32;
 
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Only the consumers (waves 4-7) load tiles: four 1-KB pieces each.
   auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
-    dma_tile<4>(base, t, Lk, dst, is_k, wave - 4, wave_u - 4u, lane);
+    if (kVt && !is_k)
+      dma_vt_tile<4, true>(base, t, Lk, ldv, dst, wave - 4, wave_u - 4u, lane);
+    else
+      dma_tile<4>(base, t, Lk, dst, is_k, wave - 4, wave_u - 4u, lane);
   };
   auto end_step = [&]() {
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");   // all but this step's 8 loads
@@ -638,6 +719,12 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     int voff[4];
     v_offsets(lane, voff);
+    auto vfrag = [&](const uint16_t *vp, int bt, int db) {
+      if constexpr (kVt)
+        return vread_t(vp, bt, db, l32, g);
+      else
+        return vread(vp, voff, bt, db);
+    };
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     float l_run0 = 0.f, l_run1 = 0.f;
     auto apply = [&](int ps, const uint16_t *vp) {
@@ -648,7 +735,7 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
       for (int j = 0; j < 4; ++j) pw4[j] = src[64 * j];
       bf16x8 vf[2][4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vf[0][db] = vread(vp, voff, 0, db);
+      for (int db = 0; db < 4; ++db) vf[0][db] = vfrag(vp, 0, db);
       // Rows whose max did not rise have alpha exactly 1.
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
         l_run0 *= alpha;
@@ -670,7 +757,7 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
         const int cur = bt & 1, nxt = cur ^ 1;
         if (bt < 3) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db) vf[nxt][db] = vread(vp, voff, bt + 1, db);
+          for (int db = 0; db < 4; ++db) vf[nxt][db] = vfrag(vp, bt + 1, db);
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -714,9 +801,10 @@ namespace {
 // orders the two launches).  The tail round then keeps every SIMD busy with
 // half a round's work.  Which launch a unit lands in depends on H and on the
 // device, but a row's arithmetic does not.
-template <bool kLse>
+template <bool kLse, bool kVt>
 hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, float *out32,
-                        float *lse, int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
+                        float *lse, int H, int Lq, int Lk, long long kv_stride, int ldv, float scale,
+                        hipStream_t stream) {
   const int n_qtiles = (Lq + kUnitRows - 1) / kUnitRows;
   const int units = static_cast<int>(attention_grid(H, Lq));
   int dev = 0, cus = 0;
@@ -728,13 +816,13 @@ hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const int main_units = units - tail;
   const float sl2e = scale * kLog2e;
   if (main_units > 0) {
-    hipLaunchKernelGGL((attn_fwd_kernel<kLse>), dim3(main_units), dim3(512), 0, stream, q, k, v, out, out32,
-                       lse, Lq, Lk, kv_stride, n_qtiles, 0, sl2e);
+    hipLaunchKernelGGL((attn_fwd_kernel<kLse, kVt>), dim3(main_units), dim3(512), 0, stream, q, k, v, out, out32,
+                       lse, Lq, Lk, kv_stride, ldv, n_qtiles, 0, sl2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (tail > 0) {
-    hipLaunchKernelGGL((attn_tail_kernel<kLse>), dim3(2 * tail), dim3(512), 0, stream, q, k, v, out, out32,
-                       lse, Lq, Lk, kv_stride, n_qtiles, main_units, sl2e);
+    hipLaunchKernelGGL((attn_tail_kernel<kLse, kVt>), dim3(2 * tail), dim3(512), 0, stream, q, k, v, out, out32,
+                       lse, Lq, Lk, kv_stride, ldv, n_qtiles, main_units, sl2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -744,13 +832,19 @@ hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out, int H,
                             int L, float scale, hipStream_t stream) {
-  return launch_split<false>(q, k, v, out, nullptr, nullptr, H, L, L, static_cast<long long>(L) * D, scale,
-                             stream);
+  return launch_split<false, false>(q, k, v, out, nullptr, nullptr, H, L, L, static_cast<long long>(L) * D, 0,
+                                    scale, stream);
+}
+
+hipError_t launch_attention_vt(const uint16_t *q, const uint16_t *k, const uint16_t *vt, uint16_t *out, int H,
+                               int L, int ldv, float scale, hipStream_t stream) {
+  return launch_split<false, true>(q, k, vt, out, nullptr, nullptr, H, L, L, static_cast<long long>(L) * D, ldv,
+                                   scale, stream);
 }
 
 hipError_t launch_attention_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v, float *out, float *lse,
                                 int H, int Lq, int Lk, long long kv_stride, float scale, hipStream_t stream) {
-  return launch_split<true>(q, k, v, nullptr, out, lse, H, Lq, Lk, kv_stride, scale, stream);
+  return launch_split<true, false>(q, k, v, nullptr, out, lse, H, Lq, Lk, kv_stride, 0, scale, stream);
 }
 
 // Merge of P partial results: one 32-lane half-wave per (head, row); lane

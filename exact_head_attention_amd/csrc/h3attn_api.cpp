@@ -89,6 +89,25 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 
+int h3_attention_vt(const void *q, const void *k, const void *vt, void *out, int H, int L, int ldv, int D,
+                    float scale, void *stream) {
+  if (!q || !k || !vt || !out) return H3_ERR_NULL;
+  if (!shape_ok(H, L) || L > H3ATTN_MAX_ATTENTION_L || h3::attention_grid(H, L) >= (int64_t{1} << 31) ||
+      ldv < L || ldv > H3ATTN_MAX_ATTENTION_L)
+    return H3_ERR_SHAPE;
+  if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out) || (ldv % 8) != 0) return H3_ERR_ALIGN;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
+  const uint64_t vt_bytes = static_cast<uint64_t>(H) * D * ldv * 2;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, vt, vt_bytes))
+    return H3_ERR_ALIAS;
+  hipError_t e = h3::launch_attention_vt(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                         static_cast<const uint16_t *>(vt), static_cast<uint16_t *>(out), H, L, ldv,
+                                         scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
 int h3_attention_lse(const void *q, const void *k, const void *v, float *out, float *lse, int H, int Lq,
                      int Lk, long long kv_head_stride, int D, float scale, void *stream) {
   if (!q || !k || !v || !out || !lse) return H3_ERR_NULL;
@@ -155,23 +174,25 @@ int h3_rope_tables(const int *positions, int L, int D, double theta,
   return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 
-// Shared checks of the two projection entry points (elem = bytes per hidden
-// element; scales = the fp8 form's two device scalars, else null).
+// Shared checks of the projection entry points (scales = the fp8 form's two
+// device scalars, else null; ldv = 0 for v as [H][L][D], else v's row length
+// as [H][D][ldv]).
 static int check_qkv_proj(const void *x, const void *wq, const void *wk, const void *wv, const float *x_scale,
                           const float *w_scale, bool fp8, const float *gamma_q, const float *gamma_k,
                           const float *cos, const float *sin, void *q, void *k, void *v, int H, int L,
-                          int hidden, int D, float eps) {
+                          int hidden, int D, float eps, int ldv) {
   if (!x || !wq || !wk || !wv || !gamma_q || !gamma_k || !cos || !sin || !q || !k || !v) return H3_ERR_NULL;
   if (fp8 && (!x_scale || !w_scale)) return H3_ERR_NULL;
   const int step = fp8 ? 64 : 32;   // hidden elements per 64 bytes: half of the kernel's 128-byte step
   if (!shape_ok(H, L) || hidden < step || hidden % step != 0 || hidden > (1 << 20) ||
-      h3::qkv_proj_grid(H, L) >= (int64_t{1} << 31))
+      h3::qkv_proj_grid(H, L) >= (int64_t{1} << 31) || (ldv != 0 && (ldv < L || ldv > H3ATTN_MAX_ATTENTION_L)))
     return H3_ERR_SHAPE;
   if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
   const void *ptrs[] = {x, wq, wk, wv, gamma_q, gamma_k, cos, sin, q, k, v};
   for (const void *p : ptrs)
     if (!aligned16(p)) return H3_ERR_ALIGN;
   if (fp8 && (!aligned4(x_scale) || !aligned4(w_scale))) return H3_ERR_ALIGN;
+  if (ldv % 8 != 0) return H3_ERR_ALIGN;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return H3_ERR_VALUE;
   const uint64_t elem = fp8 ? 1 : 2;
   const uint64_t x_bytes = static_cast<uint64_t>(L) * hidden * elem;
@@ -179,31 +200,61 @@ static int check_qkv_proj(const void *x, const void *wq, const void *wk, const v
   const uint64_t t_bytes = static_cast<uint64_t>(H) * L * D * 2;
   const uint64_t tab_bytes = static_cast<uint64_t>(L) * (D / 2) * 4;
   const void *outs[] = {q, k, v};
+  const uint64_t out_bytes[] = {t_bytes, t_bytes, ldv ? static_cast<uint64_t>(H) * D * ldv * 2 : t_bytes};
   const struct { const void *p; uint64_t n; } ins[] = {
       {x, x_bytes}, {wq, w_bytes}, {wk, w_bytes}, {wv, w_bytes}, {gamma_q, D * 4u}, {gamma_k, D * 4u},
       {cos, tab_bytes}, {sin, tab_bytes}, {x_scale, fp8 ? 4u : 0u}, {w_scale, fp8 ? 4u : 0u}};
   for (int i = 0; i < 3; ++i) {
     for (const auto &in : ins)
-      if (in.p && overlaps(outs[i], t_bytes, in.p, in.n)) return H3_ERR_ALIAS;
+      if (in.p && overlaps(outs[i], out_bytes[i], in.p, in.n)) return H3_ERR_ALIAS;
     for (int j = i + 1; j < 3; ++j)
-      if (overlaps(outs[i], t_bytes, outs[j], t_bytes)) return H3_ERR_ALIAS;
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return H3_ERR_ALIAS;
   }
   return H3_OK;
+}
+
+static int qkv_proj_bf16(const void *x, const void *wq, const void *wk, const void *wv, const float *gamma_q,
+                         const float *gamma_k, const float *cos, const float *sin, void *q, void *k, void *v, int H,
+                         int L, int ldv, int hidden, int D, float eps, void *stream) {
+  const int st = check_qkv_proj(x, wq, wk, wv, nullptr, nullptr, false, gamma_q, gamma_k, cos, sin, q, k, v, H,
+                                L, hidden, D, eps, ldv);
+  if (st != H3_OK) return st;
+  hipError_t e = h3::launch_qkv_proj_qknorm_rope(
+      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wq), static_cast<const uint16_t *>(wk),
+      static_cast<const uint16_t *>(wv), gamma_q, gamma_k, cos, sin, static_cast<uint16_t *>(q),
+      static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps, ldv,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+}
+
+static int qkv_proj_fp8(const void *x, const float *x_scale, const void *wq, const void *wk, const void *wv,
+                        const float *w_scale, const float *gamma_q, const float *gamma_k, const float *cos,
+                        const float *sin, void *q, void *k, void *v, int H, int L, int ldv, int hidden, int D,
+                        float eps, void *stream) {
+  const int st = check_qkv_proj(x, wq, wk, wv, x_scale, w_scale, true, gamma_q, gamma_k, cos, sin, q, k, v, H,
+                                L, hidden, D, eps, ldv);
+  if (st != H3_OK) return st;
+  hipError_t e = h3::launch_qkv_proj_fp8_qknorm_rope(
+      static_cast<const uint8_t *>(x), x_scale, static_cast<const uint8_t *>(wq),
+      static_cast<const uint8_t *>(wk), static_cast<const uint8_t *>(wv), w_scale, gamma_q, gamma_k, cos, sin,
+      static_cast<uint16_t *>(q), static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps, ldv,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
 }
 
 int h3_qkv_proj_qknorm_rope(const void *x, const void *wq, const void *wk, const void *wv,
                             const float *gamma_q, const float *gamma_k, const float *cos,
                             const float *sin, void *q, void *k, void *v, int H, int L,
                             int hidden, int D, float eps, void *stream) {
-  const int st = check_qkv_proj(x, wq, wk, wv, nullptr, nullptr, false, gamma_q, gamma_k, cos, sin, q, k, v, H,
-                                L, hidden, D, eps);
-  if (st != H3_OK) return st;
-  hipError_t e = h3::launch_qkv_proj_qknorm_rope(
-      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wq), static_cast<const uint16_t *>(wk),
-      static_cast<const uint16_t *>(wv), gamma_q, gamma_k, cos, sin, static_cast<uint16_t *>(q),
-      static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps,
-      static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+  return qkv_proj_bf16(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, q, k, v, H, L, 0, hidden, D, eps, stream);
+}
+
+int h3_qkv_proj_qknorm_rope_vt(const void *x, const void *wq, const void *wk, const void *wv,
+                               const float *gamma_q, const float *gamma_k, const float *cos,
+                               const float *sin, void *q, void *k, void *vt, int H, int L, int ldv,
+                               int hidden, int D, float eps, void *stream) {
+  if (ldv < 1) return H3_ERR_SHAPE;
+  return qkv_proj_bf16(x, wq, wk, wv, gamma_q, gamma_k, cos, sin, q, k, vt, H, L, ldv, hidden, D, eps, stream);
 }
 
 int h3_qkv_proj_fp8_qknorm_rope(const void *x, const float *x_scale, const void *wq, const void *wk,
@@ -211,15 +262,18 @@ int h3_qkv_proj_fp8_qknorm_rope(const void *x, const float *x_scale, const void 
                                 const float *gamma_k, const float *cos, const float *sin, void *q,
                                 void *k, void *v, int H, int L, int hidden, int D, float eps,
                                 void *stream) {
-  const int st = check_qkv_proj(x, wq, wk, wv, x_scale, w_scale, true, gamma_q, gamma_k, cos, sin, q, k, v, H,
-                                L, hidden, D, eps);
-  if (st != H3_OK) return st;
-  hipError_t e = h3::launch_qkv_proj_fp8_qknorm_rope(
-      static_cast<const uint8_t *>(x), x_scale, static_cast<const uint8_t *>(wq),
-      static_cast<const uint8_t *>(wk), static_cast<const uint8_t *>(wv), w_scale, gamma_q, gamma_k, cos, sin,
-      static_cast<uint16_t *>(q), static_cast<uint16_t *>(k), static_cast<uint16_t *>(v), H, L, hidden, eps,
-      static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? H3_OK : H3_ERR_LAUNCH;
+  return qkv_proj_fp8(x, x_scale, wq, wk, wv, w_scale, gamma_q, gamma_k, cos, sin, q, k, v, H, L, 0, hidden, D, eps,
+                      stream);
+}
+
+int h3_qkv_proj_fp8_qknorm_rope_vt(const void *x, const float *x_scale, const void *wq, const void *wk,
+                                   const void *wv, const float *w_scale, const float *gamma_q,
+                                   const float *gamma_k, const float *cos, const float *sin, void *q,
+                                   void *k, void *vt, int H, int L, int ldv, int hidden, int D, float eps,
+                                   void *stream) {
+  if (ldv < 1) return H3_ERR_SHAPE;
+  return qkv_proj_fp8(x, x_scale, wq, wk, wv, w_scale, gamma_q, gamma_k, cos, sin, q, k, vt, H, L, ldv, hidden, D,
+                      eps, stream);
 }
 
 }  // extern "C"

@@ -7,7 +7,9 @@
 // the head_dim RMSNorm and the rotary embedding ("Tensor parallelism for
 // MiniMax-H3", PR description), fused here into the GEMM epilogue so the
 // projection never goes through HBM in between and is never rounded before
-// the norm.  Outputs are [H][L][128] bf16, the layout the attention reads.
+// the norm.  Outputs are [H][L][128] bf16, the layout the attention reads;
+// v may instead be written transposed, [H][128][ldv] with tokens contiguous
+// (the layout of h3_attention_vt).
 //
 // Work decomposition
 //   * Workgroup = (feature tile, token tile): head slots (128 output
@@ -40,6 +42,13 @@
 //     lanes and registers pairs every element of A with the same element of
 //     B, so the dot product is complete.  The two per-tensor scales multiply
 //     the fp32 accumulator before the norm.
+//   * Transposed v: a lane holds 4 consecutive features of one token, and the
+//     4 lanes of a quad hold 4 consecutive tokens.  Two exchanges inside the
+//     quad (DPP, lanes xor 1 then xor 2) transpose that 4 x 4 block, so each
+//     lane stores one feature's 4 tokens as 8 bytes, and a half-wave fills 8
+//     feature rows with 64 contiguous bytes each.  Token columns from L up to
+//     the next multiple of 8 receive the exact zeros of the token rows that
+//     read as zeros.
 //   * Blocks are ordered so that the workgroups an XCD runs at once cover
 //     8 token tiles x 4 feature tiles: each hidden-state tile and each weight
 //     tile is then read by several concurrent workgroups through that XCD's
@@ -78,6 +87,9 @@ constexpr int kChunks = kStepBytes / 16;    // 16-byte chunks per row
 constexpr int kPieceRows = 1024 / kStepBytes;   // rows per 1-KB load
 constexpr int kRing = 2;             // LDS ring depth (steps) for each of W and X
 constexpr int kE8M0One = 127;        // block-scale exponent of 1.0
+// DPP quad permutations (lane i of each quad reads lane perm[i]): xor 1 and xor 2.
+constexpr int kQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);
+constexpr int kQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes < 0 ? 0 : bytes, kBufferFlags);
@@ -112,14 +124,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 
 // kFp8 = false: bf16 operands.  kFp8 = true: e4m3 operands with per-tensor
 // scales *x_scale and *w_scale (device scalars).  C counts hidden elements.
-// Head slot j in [0, 3H) is q head j, k head j - H or v head j - 2H.
+// Head slot j in [0, 3H) is q head j, k head j - H or v head j - 2H.  ldv = 0
+// writes v as [H][L][128]; ldv > 0 (a multiple of 8, at least L) writes it as
+// [H][128][ldv].
 template <bool kFp8>
 __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void qkv_proj_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ Wq, const uint8_t *__restrict__ Wk,
     const uint8_t *__restrict__ Wv, const float *__restrict__ x_scale, const float *__restrict__ w_scale,
     const float *__restrict__ gamma_q, const float *__restrict__ gamma_k,
     const float *__restrict__ cos_t, const float *__restrict__ sin_t, uint16_t *__restrict__ Qo,
-    uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles) {
+    uint16_t *__restrict__ Ko, uint16_t *__restrict__ Vo, int H, int L, int C, float eps, int n_ttiles, int ldv) {
   constexpr int kSlots = slots_of<kFp8>();
   constexpr int kTS = ts_of<kFp8>();
   constexpr int kWaves = threads_of<kFp8>() / 64;
@@ -310,6 +324,42 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
 #pragma unroll
       for (int ts = 0; ts < kTS; ++ts) acc[fs][ts] *= sc;
   }
+  if (which == 2 && ldv > 0) {
+    // Transposed v (wave-uniform branch; every lane takes part in the
+    // exchanges, and stores are predicated afterwards).  Lane qk = l32 % 4 of
+    // a quad ends with feature f0 + qk of the quad's tokens tq .. tq+3.
+    const int qk = l32 & 3;
+    const int l8 = (L + 7) & ~7;   // columns written: the tokens plus their zero padding
+    uint16_t *vt = Vo + static_cast<size_t>(head) * D * ldv;
+#pragma unroll
+    for (int ts = 0; ts < kTS; ++ts) {
+      const int tq = t0 + th * 32 * kTS + ts * 32 + (l32 & ~3);
+#pragma unroll
+      for (int fs = 0; fs < 4; ++fs)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int f0 = 32 * fs + 8 * q4 + 4 * g;   // this lane holds features f0 .. f0+3 of token tq + qk
+          const uint32_t x = pack_bf16x2(acc[fs][ts][4 * q4], acc[fs][ts][4 * q4 + 1]);
+          const uint32_t y = pack_bf16x2(acc[fs][ts][4 * q4 + 2], acc[fs][ts][4 * q4 + 3]);
+          // Lanes xor 1: the even lane of a pair keeps features f0, f0+2 of
+          // its two tokens, the odd lane features f0+1, f0+3.
+          const uint32_t xp = __builtin_amdgcn_update_dpp(0, x, kQuadXor1, 0xF, 0xF, false);
+          const uint32_t yp = __builtin_amdgcn_update_dpp(0, y, kQuadXor1, 0xF, 0xF, false);
+          const bool odd = (qk & 1) != 0;
+          const uint32_t u = odd ? (xp >> 16) | (x & 0xFFFF0000u) : (x & 0xFFFFu) | (xp << 16);
+          const uint32_t w = odd ? (yp >> 16) | (y & 0xFFFF0000u) : (y & 0xFFFFu) | (yp << 16);
+          // Lanes xor 2: u holds feature f0 + (qk & 1), w feature f0 + 2 +
+          // (qk & 1), both for tokens tq + (qk & 2) and the next one.
+          const bool hi = (qk & 2) != 0;
+          const uint32_t got = __builtin_amdgcn_update_dpp(0, hi ? u : w, kQuadXor2, 0xF, 0xF, false);
+          uint2 out;
+          out.x = hi ? got : u;
+          out.y = hi ? w : got;
+          if (tq < l8) *reinterpret_cast<uint2 *>(vt + static_cast<size_t>(f0 + qk) * ldv + tq) = out;
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int ts = 0; ts < kTS; ++ts) {
     const int t = t0 + th * 32 * kTS + ts * 32 + l32;
@@ -360,13 +410,13 @@ int64_t qkv_proj_grid(int H, int L) {
 hipError_t launch_qkv_proj_qknorm_rope(const uint16_t *x, const uint16_t *wq, const uint16_t *wk,
                                        const uint16_t *wv, const float *gamma_q, const float *gamma_k,
                                        const float *cos_t, const float *sin_t, uint16_t *q, uint16_t *k,
-                                       uint16_t *v, int H, int L, int C, float eps, hipStream_t stream) {
+                                       uint16_t *v, int H, int L, int C, float eps, int ldv, hipStream_t stream) {
   const int n_ttiles = (L + kTok - 1) / kTok;
   const int blocks = (3 * H + slots_of<false>() - 1) / slots_of<false>() * n_ttiles;
   hipLaunchKernelGGL(qkv_proj_kernel<false>, dim3(blocks), dim3(threads_of<false>()), 0, stream,
                      reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(wq),
                      reinterpret_cast<const uint8_t *>(wk), reinterpret_cast<const uint8_t *>(wv), nullptr, nullptr,
-                     gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
+                     gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles, ldv);
   return hipGetLastError();
 }
 
@@ -374,11 +424,11 @@ hipError_t launch_qkv_proj_fp8_qknorm_rope(const uint8_t *x, const float *x_scal
                                            const uint8_t *wk, const uint8_t *wv, const float *w_scale,
                                            const float *gamma_q, const float *gamma_k, const float *cos_t,
                                            const float *sin_t, uint16_t *q, uint16_t *k, uint16_t *v, int H, int L,
-                                           int C, float eps, hipStream_t stream) {
+                                           int C, float eps, int ldv, hipStream_t stream) {
   const int n_ttiles = (L + kTok - 1) / kTok;
   const int blocks = (3 * H + slots_of<true>() - 1) / slots_of<true>() * n_ttiles;
   hipLaunchKernelGGL(qkv_proj_kernel<true>, dim3(blocks), dim3(threads_of<true>()), 0, stream, x, wq, wk, wv, x_scale,
-                     w_scale, gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles);
+                     w_scale, gamma_q, gamma_k, cos_t, sin_t, q, k, v, H, L, C, eps, n_ttiles, ldv);
   return hipGetLastError();
 }
 

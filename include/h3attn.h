@@ -97,6 +97,30 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
                  int H, int L, int D, float scale, void *stream);
 
 /*
+ * h3_attention with V given transposed: the same result, bit for bit, as
+ * h3_attention on v[h][j][d] = vt[(h*D + d)*ldv + j].  Keys are contiguous in
+ * this layout, so the kernel reads V tiles as plain 16-byte rows instead of
+ * transposing them on the LDS read, which makes the call a few per cent
+ * faster.  The layout is the one h3_qkv_proj_qknorm_rope_vt and its fp8 form
+ * write.
+ *
+ *   q, k          bf16 [H][L][D], read only.
+ *   vt            bf16 [H][D][ldv], read only: row (h, d) holds v[h][0..L-1][d]
+ *                 in columns 0..L-1.  Columns from L up to the next multiple
+ *                 of 8 are read and weighted by exact zeros, so they must be
+ *                 finite (the projection writes zeros there); later columns are
+ *                 never read.
+ *   ldv           L <= ldv <= H3ATTN_MAX_ATTENTION_L, a multiple of 8
+ *                 (H3_ERR_ALIGN otherwise).
+ *   out           bf16 [H][L][D], written; must not overlap q, k or vt.
+ *   L, scale      as for h3_attention.
+ * All tensor pointers must be 16-byte aligned.  A head split offsets vt by
+ * h0*D*ldv.
+ */
+int h3_attention_vt(const void *q, const void *k, const void *vt, void *out,
+                    int H, int L, int ldv, int D, float scale, void *stream);
+
+/*
  * Partial attention over a range of keys, with its log-sum-exp: the building
  * block for splitting the keys of one head across launches or devices
  * (context/ring parallelism, which "Tensor parallelism for MiniMax-H3" names,
@@ -209,6 +233,29 @@ int h3_qkv_proj_fp8_qknorm_rope(const void *x, const float *x_scale, const void 
                                 const float *gamma_k, const float *cos, const float *sin, void *q,
                                 void *k, void *v, int H, int L, int hidden, int D, float eps,
                                 void *stream);
+
+/*
+ * h3_qkv_proj_qknorm_rope and h3_qkv_proj_fp8_qknorm_rope with v written
+ * transposed, in the layout h3_attention_vt reads.  q and k are as in those
+ * calls; v goes to
+ *   vt[(h*D + d)*ldv + t] = v[h][t][d]     t < L,
+ * and the columns from L up to the next multiple of 8 are set to zero (their
+ * token rows of x read as zeros); later columns are left untouched.
+ *
+ *   vt            bf16 [H][D][ldv], written; must not overlap q, k or any input.
+ *   ldv           L <= ldv <= H3ATTN_MAX_ATTENTION_L, a multiple of 8
+ *                 (H3_ERR_ALIGN otherwise).
+ *   the rest      as for the call without _vt.
+ */
+int h3_qkv_proj_qknorm_rope_vt(const void *x, const void *wq, const void *wk, const void *wv,
+                               const float *gamma_q, const float *gamma_k, const float *cos,
+                               const float *sin, void *q, void *k, void *vt, int H, int L, int ldv,
+                               int hidden, int D, float eps, void *stream);
+int h3_qkv_proj_fp8_qknorm_rope_vt(const void *x, const float *x_scale, const void *wq, const void *wk,
+                                   const void *wv, const float *w_scale, const float *gamma_q,
+                                   const float *gamma_k, const float *cos, const float *sin, void *q,
+                                   void *k, void *vt, int H, int L, int ldv, int hidden, int D, float eps,
+                                   void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char *h3_status_string(int status);

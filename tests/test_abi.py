@@ -24,8 +24,10 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("h3_qknorm_rope", "h3_attention", "h3_rope_tables", "h3_attention_lse", "h3_attention_merge",
-              "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope", "h3_status_string", "h3_abi_version"):
+    for n in ("h3_qknorm_rope", "h3_attention", "h3_attention_vt", "h3_rope_tables", "h3_attention_lse",
+              "h3_attention_merge", "h3_qkv_proj_qknorm_rope", "h3_qkv_proj_fp8_qknorm_rope",
+              "h3_qkv_proj_qknorm_rope_vt", "h3_qkv_proj_fp8_qknorm_rope_vt", "h3_status_string",
+              "h3_abi_version"):
         assert n in names
 
 
@@ -72,6 +74,23 @@ def test_attention_argument_errors(B):
     assert _attn(B, o=A) == -5                             # out is q
     assert _attn(B, scale=0.0) == -6 and _attn(B, scale=-1.0) == -6
     assert _attn(B, scale=float("inf")) == -6 and _attn(B, scale=float("nan")) == -6
+
+
+def _attn_vt(B, q=A, k=A + 64 * MB, vt=A + 128 * MB, o=A + 192 * MB, H=2, L=512, ldv=512, D=128, scale=0.088):
+    return B.lib.h3_attention_vt(q, k, vt, o, H, L, ldv, D, scale, None)
+
+
+def test_attention_vt_argument_errors(B):
+    assert _attn_vt(B, vt=None) == -1 and _attn_vt(B, k=None) == -1
+    assert _attn_vt(B, H=0) == -2 and _attn_vt(B, L=0) == -2
+    assert _attn_vt(B, ldv=504) == -2                      # ldv < L
+    assert _attn_vt(B, ldv=(1 << 23) + 8) == -2            # a head's V^T past 2 GiB
+    assert _attn_vt(B, D=64) == -3
+    assert _attn_vt(B, ldv=516) == -4                      # rows not 16-byte aligned
+    assert _attn_vt(B, vt=A + 128 * MB + 8) == -4
+    assert _attn_vt(B, o=A + 128 * MB + 1024) == -5        # out inside vt
+    assert _attn_vt(B, ldv=(1 << 17) + 8) == -5            # the longer vt rows reach out
+    assert _attn_vt(B, scale=0.0) == -6 and _attn_vt(B, scale=float("nan")) == -6
 
 
 def test_prologue_argument_errors(B):
@@ -166,3 +185,29 @@ def test_qkv_proj_fp8_argument_errors(B):
     assert _qkv8(B, q=A + 11 * MB - 16) == -5               # q's end covers x_scale
     assert _qkv8(B, v=A + 10 * MB, k=A + 10 * MB + 4096) == -5
     assert _qkv8(B, eps=-1.0) == -6
+
+
+def _qkv_vt(B, x=A, wq=A + 1 * MB, wk=A + 2 * MB, wv=A + 3 * MB, gq=A + 4 * MB, gk=A + 5 * MB, c=A + 6 * MB,
+            s=A + 7 * MB, q=A + 8 * MB, k=A + 9 * MB, v=A + 10 * MB, H=2, L=512, ldv=512, C=256, D=128, eps=1e-6):
+    return B.lib.h3_qkv_proj_qknorm_rope_vt(x, wq, wk, wv, gq, gk, c, s, q, k, v, H, L, ldv, C, D, eps, None)
+
+
+def _qkv8_vt(B, x=A, xs=A + 11 * MB, wq=A + 1 * MB, wk=A + 2 * MB, wv=A + 3 * MB, ws=A + 11 * MB + 64,
+             gq=A + 4 * MB, gk=A + 5 * MB, c=A + 6 * MB, s=A + 7 * MB, q=A + 8 * MB, k=A + 9 * MB, v=A + 10 * MB,
+             H=2, L=512, ldv=512, C=256, D=128, eps=1e-6):
+    return B.lib.h3_qkv_proj_fp8_qknorm_rope_vt(x, xs, wq, wk, wv, ws, gq, gk, c, s, q, k, v, H, L, ldv, C, D, eps,
+                                                None)
+
+
+def test_qkv_proj_vt_argument_errors(B):
+    assert _qkv_vt(B, v=None) == -1 and _qkv_vt(B, x=None) == -1
+    assert _qkv_vt(B, ldv=0) == -2 and _qkv_vt(B, ldv=504) == -2 and _qkv_vt(B, ldv=(1 << 23) + 8) == -2
+    assert _qkv_vt(B, C=48) == -2
+    assert _qkv_vt(B, ldv=524) == -4                       # rows not 16-byte aligned
+    assert _qkv_vt(B, ldv=4096, q=A + 11 * MB) == -5       # 2 MB of vt rows reach q
+    assert _qkv_vt(B, eps=0.0) == -6
+    assert _qkv8_vt(B, xs=None) == -1 and _qkv8_vt(B, v=None) == -1
+    assert _qkv8_vt(B, ldv=8) == -2 and _qkv8_vt(B, C=96) == -2
+    assert _qkv8_vt(B, ldv=514) == -4
+    assert _qkv8_vt(B, ldv=8192) == -5                     # 4 MB of vt rows reach x_scale
+    assert _qkv8_vt(B, eps=float("nan")) == -6
