@@ -119,6 +119,13 @@ def test_binding_rejects_cpu_tensors(B):
         B.attention(q, q, q)
     with pytest.raises(ValueError):
         B.attention(torch.zeros(1, 4, 64, dtype=torch.bfloat16), q, q)
+    vt = torch.zeros(1, 128, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        B.attention_vt(q, q, vt)
+    with pytest.raises(ValueError):
+        B.attention_vt(q, q, torch.zeros(1, 128, 2, dtype=torch.bfloat16))   # ldv < L
+    with pytest.raises(ValueError):
+        B.attention_vt(q, q, torch.zeros(2, 128, 8, dtype=torch.bfloat16))   # head count
 
 
 def _lse(B, q=A, k=A + 64 * MB, v=A + 128 * MB, o=A + 192 * MB, lse=A + 320 * MB, H=2, Lq=512, Lk=256,
