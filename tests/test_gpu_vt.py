@@ -80,8 +80,9 @@ def test_attention_vt_vs_oracle(gpu_lib):
 
 # On a 256-CU part: (1, 4096) runs every unit in the tail launch; (7, 32768),
 # one rank's share at world size 8, three full rounds plus a tail launch;
-# (10, 6000) one partial round in the main launch only.
-@pytest.mark.parametrize("H,L", [(1, 4096), (7, 32768), (10, 6000)])
+# (10, 6000) one partial round in the main launch only; (56, 4096) all 56
+# heads at once, again three rounds plus a tail.
+@pytest.mark.parametrize("H,L", [(1, 4096), (7, 32768), (10, 6000), (56, 4096)])
 def test_attention_vt_launch_shapes_bit_identical(gpu_lib, H, L):
     q, k, v = _raw(H, L, seed=H * 100003 + L)
     vt = _transposed(v, L, seed=1)
