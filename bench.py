@@ -636,9 +636,11 @@ def main():
     sclk = read_sclk_summary(w.name)
     if sclk is not None:
         # The published peak assumes 2.4 GHz; the chip holds a lower clock
-        # under this load (measured with counters, see the SQ summary).
-        rec["roofline"]["measured_sclk_ghz"] = sclk
-        rec["roofline"]["frac_at_measured_sclk"] = round(
+        # under this load.  This clock comes from the committed SQ counter
+        # summary (an earlier profiling run, possibly on another box), not
+        # from this run, and is labelled so.
+        rec["roofline"]["profile_sclk_ghz"] = sclk
+        rec["roofline"]["frac_at_profile_sclk"] = round(
             att_tflops / (BF16_MFMA_PEAK_TFLOPS * sclk / PEAK_CLOCK_GHZ), 4)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
