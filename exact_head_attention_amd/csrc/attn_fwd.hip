@@ -432,8 +432,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     ka[0][1] = kread(kp, koff, 1, 0);
     const uint16_t *vp = v_lds[R];
     bf16x8 vf[2][4];
-    // (1)
+    // (1)  A wave that rescales has extra work before the barrier: it runs
+    // the rest of its step at a raised issue priority (s_setprio 1, reset
+    // after the barrier), so the other wave on its SIMD yields to it
+    // (same-box A/B: +0.9% at H = 7, +0.6% at H = 56; bits unchanged).
     if (__builtin_amdgcn_ballot_w64(mx > m_run) != 0) {
+      __builtin_amdgcn_s_setprio(1);
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -516,6 +520,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     // (4)
     dma_wait_all_but_one_pair();
     asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_s_setprio(0);
     // This wave's P.V reads of this step land here at the latest, whatever
     // the compiler does with the products that consume them.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
