@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "h3attn_internal.h"
@@ -799,6 +800,21 @@ int64_t attention_grid(int H, int L) {
 
 namespace {
 
+// Compute units of the current device, queried once per device and cached
+// (the count never changes while the process runs; racing first queries
+// store the same value).
+hipError_t device_cu_count(int *cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && (*cus = cached[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) cached[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 // Main launch + tail launch.  Units run in rounds of one 8-wave workgroup per
 // CU; when the last round would leave at least half the CUs idle (r <= CUs/2
 // units left over), those r units instead run as 2r attn_tail_kernel
@@ -812,9 +828,8 @@ hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         hipStream_t stream) {
   const int n_qtiles = (Lq + kUnitRows - 1) / kUnitRows;
   const int units = static_cast<int>(attention_grid(H, Lq));
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = device_cu_count(&cus);
   if (e != hipSuccess) return e;
   const int rem = cus > 0 ? units % cus : 0;
   const int tail = (cus > 0 && rem <= cus / 2) ? rem : 0;

@@ -28,6 +28,12 @@ bool shape_ok(int H, int L) {
   return rows < (int64_t{1} << 31);
 }
 
+// The attention kernels work in base 2 with scale * log2(e) folded into one
+// fp32 factor; a scale whose factor overflows fp32 is rejected.
+bool scale_ok(float scale) {
+  return scale > 0.0f && std::isfinite(scale) && std::isfinite(scale * 1.4426950408889634f);
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,7 +85,7 @@ int h3_attention(const void *q, const void *k, const void *v, void *out,
     return H3_ERR_SHAPE;
   if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return H3_ERR_ALIGN;
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  if (!scale_ok(scale)) return H3_ERR_VALUE;
   const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
     return H3_ERR_ALIAS;
@@ -97,7 +103,7 @@ int h3_attention_vt(const void *q, const void *k, const void *vt, void *out, int
     return H3_ERR_SHAPE;
   if (D != H3ATTN_HEAD_DIM) return H3_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out) || (ldv % 8) != 0) return H3_ERR_ALIGN;
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  if (!scale_ok(scale)) return H3_ERR_VALUE;
   const uint64_t bytes = static_cast<uint64_t>(H) * L * D * 2;
   const uint64_t vt_bytes = static_cast<uint64_t>(H) * D * ldv * 2;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, vt, vt_bytes))
@@ -119,7 +125,7 @@ int h3_attention_lse(const void *q, const void *k, const void *v, float *out, fl
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(lse) ||
       (kv_head_stride % 8) != 0)
     return H3_ERR_ALIGN;
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return H3_ERR_VALUE;
+  if (!scale_ok(scale)) return H3_ERR_VALUE;
   const uint64_t q_bytes = static_cast<uint64_t>(H) * Lq * D * 2;
   const uint64_t kv_bytes = (static_cast<uint64_t>(H - 1) * kv_head_stride + static_cast<uint64_t>(Lk) * D) * 2;
   const uint64_t out_bytes = static_cast<uint64_t>(H) * Lq * D * 4;

@@ -29,26 +29,15 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef H3_PRO_LNT
-#define H3_PRO_LNT 1
-#endif
-#ifndef H3_PRO_SNT
-#define H3_PRO_SNT 1
-#endif
 // q and k rows are touched exactly once: stream them past the caches.
 __device__ __forceinline__ uint4 load_stream(const uint16_t *p) {
-  if (H3_PRO_LNT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
-  return *reinterpret_cast<const uint4 *>(p);
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
 }
 __device__ __forceinline__ void store_stream(uint16_t *p, uint4 v) {
-  if (H3_PRO_SNT) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
-  else *reinterpret_cast<uint4 *>(p) = v;
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
 }
 
-#ifndef H3_PRO_TPB
-#define H3_PRO_TPB 16
-#endif
-constexpr int kTokensPerBlock = H3_PRO_TPB;   // 16 lanes per token
+constexpr int kTokensPerBlock = 16;   // 16 lanes per token
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -61,13 +50,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// Sum over the 16 lanes of a DPP row; every lane gets the total.
+// Sum over the 16 lanes of a DPP row, as a butterfly: lanes exchange with
+// their partner at distance 1, 2 (quad_perm), then across the half-row
+// (row_half_mirror) and across the row (row_mirror).  At every stage both
+// partners add the same two values, and fp32 addition is commutative, so all
+// 16 lanes end with the same bits: the whole token is normalised by one r.
 __device__ __forceinline__ float row16_sum(float v) {
-  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));   // row_mirror
   return v;
 }
 

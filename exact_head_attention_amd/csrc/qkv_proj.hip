@@ -172,7 +172,7 @@ __global__ __launch_bounds__(threads_of<kFp8>(), threads_of<kFp8>() / 256) void 
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + static_cast<size_t>(t0) * row_bytes, tok_rows * row_bytes);
 
   // Steps go from global memory straight into LDS (buffer loads with the
-  // LDS-destination bit), three steps ahead of the one being multiplied.
+  // LDS-destination bit), one step ahead of the one being multiplied.
   // A load writes rows 8n .. 8n+7 of the step's weight rows or 256 token
   // rows as one contiguous kilobyte: lane i lands in row 8n + i/8 at
   // physical chunk i%8 and fetches the row's logical chunk (i%8) ^ swizzle.

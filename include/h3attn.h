@@ -50,8 +50,8 @@ typedef enum {
   H3_ERR_UNSUPPORTED = -3, /* D != 128                                            */
   H3_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned             */
   H3_ERR_ALIAS = -5,       /* out overlaps q, k or v; q overlaps k; cos overlaps sin */
-  H3_ERR_VALUE = -6,       /* eps <= 0 or not finite; scale <= 0 or not finite;   */
-                           /* theta <= 1 or not finite                            */
+  H3_ERR_VALUE = -6,       /* eps <= 0 or not finite; scale <= 0, not finite, or  */
+                           /* scale*log2(e) not finite; theta <= 1 or not finite  */
   H3_ERR_LAUNCH = -7       /* the HIP runtime refused the launch                  */
 } h3_status;
 
@@ -83,14 +83,21 @@ int h3_qknorm_rope(void *q, void *k, const float *gamma_q, const float *gamma_k,
 /*
  * Exact, unmasked, non-causal attention per head:
  *   out[h][i][:] = sum_j softmax_j(scale * <q[h][i], k[h][j]>) * v[h][j][:]
- * over all L keys of head h.  bf16 inputs, bf16 MFMA products with fp32
- * accumulation, online softmax in fp32, output rounded once to bf16.  Any
- * 1 <= L <= H3ATTN_MAX_ATTENTION_L is accepted; a partial last tile is
- * predicated, never padded.
+ * over all L keys of head h.  This is what each Ulysses rank computes for its
+ * 56/world_size heads over the whole packed sequence ("buqi-minimax-h3-
+ * multigpu", How it works), exactly, with nothing approximated or masked
+ * (the same README, On accuracy); the packed video+audio sequence takes no
+ * mask and its real lengths are not tile multiples ("Tensor parallelism for
+ * MiniMax-H3", whn09's FYI for anyone else on Neuron eager).
+ * bf16 inputs, bf16 MFMA products with fp32 accumulation, online softmax in
+ * fp32, output rounded once to bf16.  Any 1 <= L <= H3ATTN_MAX_ATTENTION_L is
+ * accepted; a partial last tile is predicated, never padded.
  *
- *   q, k, v       bf16 [H][L][D], read only.
+ *   q, k, v       bf16 [H][L][D], read only; finite values.
  *   out           bf16 [H][L][D], written; must not overlap q, k or v.
- *   scale         > 0 and finite (MiniMax-H3 uses 1/sqrt(128)).
+ *   scale         > 0 and finite, with scale * log2(e) finite in fp32
+ *                 (H3_ERR_VALUE otherwise); MiniMax-H3 uses 1/sqrt(128).  The
+ *                 caller keeps every scale * <q, k> finite in fp32.
  * All tensor pointers must be 16-byte aligned.
  */
 int h3_attention(const void *q, const void *k, const void *v, void *out,
@@ -138,7 +145,7 @@ int h3_attention_vt(const void *q, const void *k, const void *vt, void *out,
  *   out           fp32 [H][Lq][D], written.      lse  fp32 [H][Lq], written.
  *   Lq, Lk        1 .. H3ATTN_MAX_ATTENTION_L;  kv_head_stride >= Lk*D and a
  *                 multiple of 8 elements.
- *   scale         > 0 and finite.
+ *   scale         as for h3_attention.
  * q, k, v, out must be 16-byte aligned; out and lse must not overlap the
  * inputs or each other.  Bit-identical per head for any head split.
  */

@@ -74,6 +74,15 @@ def test_attention_argument_errors(B):
     assert _attn(B, o=A) == -5                             # out is q
     assert _attn(B, scale=0.0) == -6 and _attn(B, scale=-1.0) == -6
     assert _attn(B, scale=float("inf")) == -6 and _attn(B, scale=float("nan")) == -6
+    # scale * log2(e) must stay finite in fp32: 3e38 is a finite float whose
+    # product with log2(e) is not; 2e38 still is.
+    assert _attn(B, scale=3e38) == -6
+    assert _attn(B, scale=2e38, o=A) == -5                 # passes the value check, fails later
+
+
+def test_scale_range_is_shared_by_every_attention_call(B):
+    assert _attn_vt(B, scale=3e38) == -6
+    assert _lse(B, scale=3e38) == -6
 
 
 def _attn_vt(B, q=A, k=A + 64 * MB, vt=A + 128 * MB, o=A + 192 * MB, H=2, L=512, ldv=512, D=128, scale=0.088):

@@ -11,29 +11,31 @@ import pytest
 
 import oracle
 from exact_head_attention_amd import inputs as I
-from tests.gpu_helpers import ATTN_TOL, bits, device_inputs, host_inputs, row_rel_err, to_dev
+from tests.gpu_helpers import (attention_errors, bits, check_attention_errors, device_inputs, host_inputs,
+                               merge_errors, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 
-def _attention_vs_oracle(gpu_lib, q, k, v, scale, rows_per_head=None, label=""):
-    """Run h3_attention on device tensors and compare with the oracle fed the
-    same bf16 bits.  rows_per_head: None (all rows) or one index array per head."""
+def _attention_vs_oracle(gpu_lib, q, k, v, scale, rows_per_head=None, label="", out=None):
+    """Run h3_attention on device tensors (unless out is given) and compare
+    with the oracle fed the same bf16 bits, on the row and element bars.
+    rows_per_head: None (all rows) or one index array per head."""
     import torch
-    out = gpu_lib.attention(q, k, v, scale=scale)
+    if out is None:
+        out = gpu_lib.attention(q, k, v, scale=scale)
     torch.cuda.synchronize()
     qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
     H = qb.shape[0]
-    worst = 0.0
+    parts = []
     for h in range(H):
         rows = np.arange(qb.shape[1]) if rows_per_head is None else rows_per_head[h]
         ref = oracle.attention_head(oracle.bf16_to_f64(qb[h, rows]), oracle.bf16_to_f64(kb[h]),
                                     oracle.bf16_to_f64(vb[h]), scale)
-        err = row_rel_err(ob[h, rows], ref)
-        worst = max(worst, float(err.max()))
-        assert np.all(np.isfinite(oracle.bf16_to_f64(ob[h, rows])))
-    print(f"{label}: max row rel err {worst:.3e}")
-    assert worst <= ATTN_TOL
+        got = oracle.bf16_to_f64(ob[h, rows])
+        assert np.all(np.isfinite(got))
+        parts.append(attention_errors(got, ref))
+    check_attention_errors(label, merge_errors(parts))
     return out
 
 
@@ -52,6 +54,34 @@ def test_attention_ragged_lengths_all_rows(gpu_lib, L):
     _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), label=f"L={L}")
 
 
+# Main-launch-only shapes: 10 heads of 20 query tiles are 200 units, which
+# run as one partial round of the full-round kernel (no tail launch), with the
+# last key tile in each position of the 4-step loop (77, 78, 79, 80 tiles).
+# Every row against the oracle, and h3_attention_vt bit for bit.
+@pytest.mark.parametrize("L", [4900, 4950, 5050, 5100])
+def test_attention_main_launch_ragged_all_rows(gpu_lib, L):
+    import torch
+    q, k, v = _raw(10, L, seed=500 + L)
+    out = _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), label=f"main launch H=10 L={L}")
+    l8 = (L + 7) // 8 * 8
+    vt = torch.zeros((10, 128, l8), dtype=torch.bfloat16, device=q.device)
+    vt[:, :, :L] = v.transpose(1, 2)
+    out_vt = gpu_lib.attention_vt(q, k, vt, scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(out_vt, out), "h3_attention_vt differs from h3_attention"
+
+
+# The scale reaches the kernel as a run-time argument: two values other than
+# 1/sqrt(128), a flat softmax (0.03: logit sd ~0.34) and a peaky one (0.3:
+# logit sd ~3.4), through the main launch (H = 10, L = 4900: 200 units) and the
+# tail launch (H = 3, L = 1000: 12 units).
+@pytest.mark.parametrize("scale", [0.03, 0.3])
+@pytest.mark.parametrize("H,L", [(10, 4900), (3, 1000)])
+def test_attention_nondefault_scale(gpu_lib, scale, H, L):
+    q, k, v = _raw(H, L, seed=700 + L)
+    _attention_vs_oracle(gpu_lib, q, k, v, scale, label=f"scale={scale} H={H} L={L}")
+
+
 def test_attention_tiny_end_to_end(gpu_lib):
     """Prologue then attention on the tiny workload, every row; the oracle
     attention consumes the GPU prologue's bf16 output, and the all-oracle
@@ -67,9 +97,7 @@ def test_attention_tiny_end_to_end(gpu_lib):
     _, qb = oracle.qknorm_rope(x["q"], x["gamma_q"], c_ref, s_ref, x["eps"])
     _, kb = oracle.qknorm_rope(x["k"], x["gamma_k"], c_ref, s_ref, x["eps"])
     ref = oracle.attention(qb, kb, x["v"], x["scale"])
-    err = row_rel_err(bits(out).reshape(-1, 128), ref.reshape(-1, 128))
-    print(f"tiny all-oracle chain: max row rel err {err.max():.3e}")
-    assert err.max() <= ATTN_TOL
+    check_attention_errors("tiny all-oracle chain", attention_errors(oracle.bf16_to_f64(bits(out)), ref))
 
 
 def test_attention_special_cases(gpu_lib):
@@ -85,12 +113,11 @@ def test_attention_special_cases(gpu_lib):
     k_same = k[:, :1].expand(1, L, 128).contiguous()
     out = gpu_lib.attention(q, k_same, v)
     mean = oracle.bf16_to_f64(bits(v))[0].mean(axis=0)
-    err = row_rel_err(bits(out)[0], np.tile(mean, (L, 1)))
-    assert err.max() <= ATTN_TOL, err.max()
+    check_attention_errors("identical keys", attention_errors(oracle.bf16_to_f64(bits(out)[0]), np.tile(mean, (L, 1))))
     v_const = v[:, :1].expand(1, L, 128).contiguous()
     out = gpu_lib.attention(q, k, v_const)
-    err = row_rel_err(bits(out)[0], np.tile(oracle.bf16_to_f64(bits(v_const))[0, 0], (L, 1)))
-    assert err.max() <= ATTN_TOL, err.max()
+    const = np.tile(oracle.bf16_to_f64(bits(v_const))[0, 0], (L, 1))
+    check_attention_errors("constant V", attention_errors(oracle.bf16_to_f64(bits(out)[0]), const))
 
 
 @pytest.mark.parametrize("L", [4900, 5000])
@@ -236,7 +263,6 @@ def test_attention_max_length(gpu_lib):
     rows = np.unique(np.concatenate([[0, q_base - 1], rng.choice(q_base, 62, replace=False)]))
     ref = oracle.attention_head(oracle.bf16_to_f64(qb[rows]), oracle.bf16_to_f64(kb), oracle.bf16_to_f64(vb),
                                 1 / math.sqrt(128))
-    err = row_rel_err(bits(out[0, :q_base])[rows], ref)
-    last = row_rel_err(bits(out[0, L - q_base:])[rows], ref)
-    print(f"L=2^23: max row rel err {max(err.max(), last.max()):.3e}")
-    assert err.max() <= ATTN_TOL and last.max() <= ATTN_TOL
+    first = attention_errors(oracle.bf16_to_f64(bits(out[0, :q_base])[rows]), ref)
+    last = attention_errors(oracle.bf16_to_f64(bits(out[0, L - q_base:])[rows]), ref)
+    check_attention_errors("L=2^23", merge_errors([first, last]))

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from exact_head_attention_amd import inputs as I
-from tests.gpu_helpers import ATTN_TOL, bits, host_inputs, row_rel_err, to_dev
+from tests.gpu_helpers import attention_errors, bits, check_attention_errors, host_inputs, merge_errors, to_dev
 
 pytestmark = pytest.mark.gpu
 LSE_TOL = 2e-3
@@ -25,28 +25,41 @@ def _raw(H, L, seed, mult=1.0):
             for _ in range(3)]
 
 
-def _rel_rows(got, ref):
-    return np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+def _lse_vs_oracle(gpu_lib, q, k, v, s, label):
+    """h3_attention_lse on device tensors: out (fp32, no output rounding) on
+    the row and element bars, lse absolutely, every row."""
+    import torch
+    out, lse = gpu_lib.attention_lse(q, k, v, scale=s)
+    torch.cuda.synchronize()
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    parts, lerr = [], 0.0
+    for h in range(qb.shape[0]):
+        ref, ref_lse = oracle.attention_lse_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h]),
+                                                 oracle.bf16_to_f64(vb[h]), s)
+        parts.append(attention_errors(out[h].double().cpu().numpy(), ref, rounded=False))
+        lerr = max(lerr, float(np.abs(lse[h].double().cpu().numpy() - ref_lse).max()))
+    print(f"{label}: max |dlse| {lerr:.2e}")
+    check_attention_errors(label, merge_errors(parts))
+    assert lerr <= LSE_TOL
 
 
 @pytest.mark.parametrize("Lq,j0,j1", [(300, 0, 300), (257, 100, 1000), (64, 999, 1000), (1000, 0, 1)])
 def test_attention_lse_range_vs_oracle(gpu_lib, Lq, j0, j1):
     """Queries against a key range given as a pointer offset into a larger
     tensor; out (fp32) and lse against the oracle on every row."""
-    import torch
     q, _, _ = _raw(2, Lq, seed=31 + Lq)
     _, kf, vf = _raw(2, 1000, seed=32)
-    s = 1 / math.sqrt(128)
-    out, lse = gpu_lib.attention_lse(q, kf[:, j0:j1], vf[:, j0:j1], scale=s)
-    torch.cuda.synchronize()
-    qb, kb, vb = bits(q), bits(kf), bits(vf)
-    for h in range(2):
-        ref, ref_lse = oracle.attention_lse_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h, j0:j1]),
-                                                 oracle.bf16_to_f64(vb[h, j0:j1]), s)
-        err = _rel_rows(out[h].double().cpu().numpy(), ref)
-        lerr = np.abs(lse[h].double().cpu().numpy() - ref_lse)
-        print(f"Lq={Lq} keys [{j0},{j1}) head {h}: max row rel {err.max():.2e}, max |dlse| {lerr.max():.2e}")
-        assert err.max() <= ATTN_TOL and lerr.max() <= LSE_TOL
+    _lse_vs_oracle(gpu_lib, q, kf[:, j0:j1], vf[:, j0:j1], 1 / math.sqrt(128), f"Lq={Lq} keys [{j0},{j1})")
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.3])
+@pytest.mark.parametrize("H,L", [(10, 4900), (3, 1000)])
+def test_attention_lse_nondefault_scale(gpu_lib, scale, H, L):
+    """The partial form at two scales other than 1/sqrt(128), through the
+    main launch (200 units) and the tail launch (12 units); lse carries the
+    scale directly (ln sum exp(scale q.k))."""
+    q, k, v = _raw(H, L, seed=800 + L)
+    _lse_vs_oracle(gpu_lib, q, k, v, scale, f"lse scale={scale} H={H} L={L}")
 
 
 @pytest.mark.parametrize("cuts", [[0, 500, 1000], [0, 1, 333, 334, 1000], [0, 64, 128, 1000],
@@ -64,14 +77,13 @@ def test_split_merge_equals_full(gpu_lib, cuts):
     out, lse = gpu_lib.attention_merge(outs, lses, want_lse=True)
     torch.cuda.synchronize()
     qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
-    worst = 0.0
+    parts = []
     for h in range(3):
         ref, ref_lse = oracle.attention_lse_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h]),
                                                  oracle.bf16_to_f64(vb[h]), s)
-        worst = max(worst, float(row_rel_err(ob[h], ref).max()))
+        parts.append(attention_errors(oracle.bf16_to_f64(ob[h]), ref))
         assert np.abs(lse[h].double().cpu().numpy() - ref_lse).max() <= LSE_TOL
-    print(f"cuts {cuts}: merged max row rel {worst:.2e}")
-    assert worst <= ATTN_TOL
+    check_attention_errors(f"cuts {cuts} merged", merge_errors(parts))
 
 
 def test_attention_lse_tail_workgroups_bit_identical(gpu_lib):
@@ -113,14 +125,13 @@ def test_ws8_two_halves_sampled(gpu_lib):
     out = gpu_lib.attention_merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]))
     torch.cuda.synchronize()
     qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
-    worst = 0.0
+    parts = []
     for h in range(w.H):
         rows = I.sample_rows(w, h, 4096)
         ref = oracle.attention_head(oracle.bf16_to_f64(qb[h, rows]), oracle.bf16_to_f64(kb[h]),
                                     oracle.bf16_to_f64(vb[h]), x["scale"])
-        worst = max(worst, float(row_rel_err(ob[h, rows], ref).max()))
-    print(f"ws8 split in two and merged: max row rel {worst:.2e}")
-    assert worst <= ATTN_TOL
+        parts.append(attention_errors(oracle.bf16_to_f64(ob[h, rows]), ref))
+    check_attention_errors("ws8 split in two and merged", merge_errors(parts))
 
 
 def test_attention_lse_head_splits_bit_identical(gpu_lib):

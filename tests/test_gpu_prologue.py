@@ -12,27 +12,43 @@ pytestmark = pytest.mark.gpu
 
 def _table_close(got, ref):
     """Both sides build the tables in fp64 and round once to fp32, but their
-    fp64 pow and cos may differ in the last bit.  At angles up to 1.3e5 rad
-    (position 126975) a last-bit difference is about 2^-35 absolute in the
-    angle, so an entry may differ by that much absolutely, or by one fp32 ulp
-    from the final rounding."""
+    fp64 pow and sincos may each be off by an ulp.  inv_freq = theta^(-2j/D)
+    may then differ by 2^-52 relative, and the angle pos * inv_freq by
+    2^-51 relative after its own rounding on each side; at the largest
+    position checked (126975 < 2^17, inv_freq <= 1) that is under 2^-34
+    absolute, and sincos adds 2^-52.  Rounding both fp64 values to fp32 can
+    then add one fp32 spacing.  Bound: spacing_fp32(ref) + 2^-33 (a factor
+    two over the analysis)."""
     spacing = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
     diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
-    return diff <= np.maximum(spacing, 2.0 ** -30)
+    return diff <= spacing + 2.0 ** -33
+
+
+def _tables_vs_oracle(gpu_lib, pos, theta, label):
+    import torch
+    c, s = gpu_lib.rope_tables(to_dev(pos, torch.int32), 128, theta)
+    c_ref, s_ref = oracle.rope_tables(pos, 128, theta)
+    c, s = c.cpu().numpy(), s.cpu().numpy()
+    for got, ref in ((c, c_ref), (s, s_ref)):
+        worst = float(np.abs(got.astype(np.float64) - ref.astype(np.float64)).max())
+        print(f"{label}: max |gpu - oracle| {worst:.3e} (2^{np.log2(max(worst, 2.0 ** -80)):.1f})")
+        assert np.all(_table_close(got, ref))
+        assert np.mean(got != ref) < 1e-2
+    print(f"{label}: tables identical in {np.mean(c == c_ref) * 100:.4f}% / {np.mean(s == s_ref) * 100:.4f}%")
 
 
 @pytest.mark.parametrize("name", ["tiny", "ws8", "canvas128k"])
 def test_rope_tables_match_oracle(gpu_lib, name):
-    import torch
     w = I.WORKLOADS[name]
-    pos = I.packed_positions(w.n_video, w.n_audio)
-    c, s = gpu_lib.rope_tables(to_dev(pos, torch.int32), 128, I.ROPE_THETA)
-    c_ref, s_ref = oracle.rope_tables(pos, 128, I.ROPE_THETA)
-    c, s = c.cpu().numpy(), s.cpu().numpy()
-    for got, ref in ((c, c_ref), (s, s_ref)):
-        assert np.all(_table_close(got, ref))
-        assert np.mean(got != ref) < 1e-2
-    print(f"{name}: tables identical in {np.mean(c == c_ref) * 100:.4f}% / {np.mean(s == s_ref) * 100:.4f}%")
+    _tables_vs_oracle(gpu_lib, I.packed_positions(w.n_video, w.n_audio), I.ROPE_THETA, name)
+
+
+@pytest.mark.parametrize("theta", [500.0, 1e6])
+def test_rope_tables_nondefault_theta(gpu_lib, theta):
+    """theta reaches the kernel as a run-time argument: two bases other than
+    10000 on the ws8 positions."""
+    w = I.WORKLOADS["ws8"]
+    _tables_vs_oracle(gpu_lib, I.packed_positions(w.n_video, w.n_audio), theta, f"theta={theta:g}")
 
 
 def _prologue_check(gpu_lib, x, label):
@@ -77,6 +93,19 @@ def test_prologue_parity(gpu_lib, name):
 def test_prologue_parity_canvas_x3(gpu_lib):
     """q and k drawn x3: RMSNorm removes the scale, the rows must still match."""
     _prologue_check(gpu_lib, host_inputs("canvas128k"), "canvas128k")
+
+
+@pytest.mark.parametrize("eps,rms", [(1e-3, 0.03), (1e-9, 3e-5)])
+def test_prologue_nondefault_eps(gpu_lib, eps, rms):
+    """eps reaches the kernel as a run-time argument: inputs drawn with an RMS
+    near sqrt(eps) (their mean square about eps), so that eps moves every
+    output by tens of per cent and a kernel that used another eps fails."""
+    w = I.custom_workload(H=3, L=1000, n_audio=200)
+    x = dict(I.make_inputs(w, seed=17))
+    for n in ("q", "k"):
+        x[n] = I.f32_to_bf16_bits((rms * oracle.bf16_to_f64(x[n])).astype(np.float32))
+    x["eps"] = eps
+    _prologue_check(gpu_lib, x, f"eps={eps:g}")
 
 
 @pytest.mark.parametrize("L", [1, 5, 17, 300, 32768 + 45])

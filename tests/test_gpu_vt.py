@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from exact_head_attention_amd import inputs as I
-from tests.gpu_helpers import ATTN_TOL, bits, row_rel_err, to_dev
+from tests.gpu_helpers import attention_errors, bits, check_attention_errors, merge_errors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,21 +61,31 @@ def test_attention_vt_equals_attention(gpu_lib, L):
     _same_bits(gpu_lib.attention_vt(q, k, vt), gpu_lib.attention(q, k, v), f"vt L={L} ldv={ldv}")
 
 
-def test_attention_vt_vs_oracle(gpu_lib):
-    """Every row of a ragged 3-head case against the oracle directly."""
+def _vt_vs_oracle(gpu_lib, H, L, seed, scale):
     import torch
-    H, L = 3, 777
-    q, k, v = _raw(H, L, seed=41)
-    out = gpu_lib.attention_vt(q, k, _transposed(v, 792, seed=5))
+    q, k, v = _raw(H, L, seed=seed)
+    out = gpu_lib.attention_vt(q, k, _transposed(v, (L + 7) // 8 * 8 + 8, seed=5), scale=scale)
     torch.cuda.synchronize()
     qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
-    worst = 0.0
+    parts = []
     for h in range(H):
         ref = oracle.attention_head(oracle.bf16_to_f64(qb[h]), oracle.bf16_to_f64(kb[h]),
-                                    oracle.bf16_to_f64(vb[h]), 1 / math.sqrt(128))
-        worst = max(worst, float(row_rel_err(ob[h], ref).max()))
-    print(f"vt H={H} L={L}: max row rel err {worst:.3e}")
-    assert worst <= ATTN_TOL
+                                    oracle.bf16_to_f64(vb[h]), scale)
+        parts.append(attention_errors(oracle.bf16_to_f64(ob[h]), ref))
+    check_attention_errors(f"vt H={H} L={L} scale={scale:.4g}", merge_errors(parts))
+
+
+def test_attention_vt_vs_oracle(gpu_lib):
+    """Every row of a ragged 3-head case against the oracle directly."""
+    _vt_vs_oracle(gpu_lib, 3, 777, 41, 1 / math.sqrt(128))
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.3])
+@pytest.mark.parametrize("H,L", [(10, 4900), (3, 1000)])
+def test_attention_vt_nondefault_scale(gpu_lib, scale, H, L):
+    """Two scales other than 1/sqrt(128), through the main launch (200 units)
+    and the tail launch (12 units), every row against the oracle."""
+    _vt_vs_oracle(gpu_lib, H, L, 900 + L, scale)
 
 
 # On a 256-CU part: (1, 4096) runs every unit in the tail launch; (7, 32768),

@@ -64,6 +64,6 @@ def test_counter_traffic_is_read_and_plausible():
     assert bench.read_counter_summary("ws2") is None     # recorded for ws8 only
 
 
-def test_sclk_summary_is_read():
-    sclk = bench.read_sclk_summary("ws8")
-    assert sclk is not None and 1.0 < sclk < 2.5
+def test_sq_summary_is_read():
+    sq = bench.read_sq_summary("ws8")
+    assert sq is not None and 1.0 < sq["profile_sclk_ghz"] < 2.5
