@@ -180,9 +180,12 @@ def _check8(label, got_bits, ref, ref_bits, dy, y_pre, gamma):
     assert rel <= ATTN_TOL
     # The instruction's truncation moves every element whose exact value lies
     # within about dy of a bf16 rounding boundary: ~1.2% of elements were
-    # measured to differ from RNE(exact) at H3's hidden size; a wrong operand,
-    # scale or pairing would move most of them.
-    assert mism < 0.03
+    # measured to differ from RNE(exact) at H3's hidden size (1.6-3.9% on a
+    # single 128-element token); a wrong operand, scale or pairing would move
+    # most of them.  Gate: a binomial bound at a 2% rate, four standard
+    # deviations plus three elements of slack for small counts.
+    n = got_bits.size
+    assert int(np.sum(got_bits != ref_bits)) <= 0.02 * n + 4 * np.sqrt(0.02 * n) + 3
 
 
 def _run8(gpu_lib, x, H, rows=None, label=""):
