@@ -33,7 +33,8 @@ SUMMARIES = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt")))
 def test_profiles_exist():
     names = {os.path.basename(p) for p in SUMMARIES}
     for n in ("attn_fwd_ws8_kernel_trace.txt", "attn_fwd_hbm_counters.txt", "attn_fwd_sq_counters.txt",
-              "qkv_proj_bf16_ws2_kernel_trace.txt", "qkv_proj_fp8_ws2_kernel_trace.txt"):
+              "qkv_proj_bf16_ws2_kernel_trace.txt", "qkv_proj_fp8_ws2_kernel_trace.txt",
+              "qkv_proj_bf16_ws2_sq_counters.txt", "qkv_proj_fp8_ws2_sq_counters.txt"):
         assert n in names
 
 
