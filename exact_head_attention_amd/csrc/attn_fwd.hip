@@ -557,25 +557,27 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   store_row<kLse>(o, lane_half_sum(l_run), m_run, head_off, head, qrow, Lq, g, O, O32, lse_out);
 }
 
-// Tail form: one 8-wave workgroup per 128 query rows (four 32-row groups).
-// Wave w < 4, the producer of group w, computes the scores, the running max
-// and the bf16 weights P.  Wave w + 4, its consumer (placed on the same
-// SIMD), holds O and the row sums: one step later it applies each tile's
-// rescale, sums the tile's weights and runs P.V, fed through LDS with P and
-// the per-row factor alpha.  Every row sees the same operations in the same
-// order as in attn_fwd_kernel (a rescale by exactly 1 is an identity), so
-// its bits do not change; the split only gives each SIMD two waves where
-// 128-row units would leave it one.  The producer's step is the longer one,
-// so the consumers also issue all tile loads.
+// Tail form: one workgroup per kGroups 32-row groups (kGroups = 4: 128 rows,
+// 8 waves; kGroups = 2: 64 rows, 4 waves).  Wave w < kGroups, the producer
+// of group w, computes the scores, the running max and the bf16 weights P.
+// Wave w + kGroups, its consumer, holds O and the row sums: one step later
+// it applies each tile's rescale, sums the tile's weights and runs P.V, fed
+// through LDS with P and the per-row factor alpha.  Every row sees the same
+// operations in the same order as in attn_fwd_kernel (a rescale by exactly 1
+// is an identity), so its bits do not change; the split only gives each
+// SIMD two waves (kGroups = 4: producer w and consumer w + 4 share SIMD w) or
+// one wave of its own (kGroups = 2) where a 256-row unit's 8 waves would not
+// fill the CUs.  The producer's step is the longer one, so the consumers
+// also issue all tile loads.
 //   Step kt: producers score tile kt+1 and weigh tile kt; consumers apply
 //   tile kt-1 and load V tile kt+1 (3-slot ring, read in step kt+2) and K
-//   tile kt+3 (4-slot ring, read in step kt+2), four 1-KB pieces each per
-//   tensor, waiting for all their older loads before the step's barrier.
+//   tile kt+3 (4-slot ring, read in step kt+2), 16 / kGroups 1-KB pieces each
+//   per tensor, waiting for all their older loads before the step's barrier.
 //   Every LDS access of a step has completed before that barrier
 //   (lgkmcnt(0)), so a slot may be rewritten from the step after its last
-//   read on.  K + V + P rings: 64 + 48 + 32 KB.
-template <bool kLse, bool kVt>
-__global__ __launch_bounds__(512) void attn_tail_kernel(
+//   read on.  K + V + P rings: 64 + 48 + 8 kGroups KB.
+template <bool kLse, bool kVt, int kGroups>
+__global__ __launch_bounds__(128 * kGroups) void attn_tail_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ O, float *__restrict__ O32, float *__restrict__ lse_out, int Lq, int Lk,
     long long kv_stride, int ldv, int n_qtiles, int unit_base, float scale_log2e) {
@@ -583,19 +585,20 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
   constexpr int kVSlots = 3;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kSlots][kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kVSlots][kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint4 p_lds[2][4][4 * 64];   // [slot][group][16 B piece j * 64 + lane]
-  __shared__ float a_lds[2][4][32];                                         // [slot][group][row]: alpha
+  __shared__ __attribute__((aligned(1024))) uint4 p_lds[2][kGroups][4 * 64];   // [slot][group][16 B piece j * 64 + lane]
+  __shared__ float a_lds[2][kGroups][32];                                         // [slot][group][row]: alpha
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int grp = wave & 3;
+  const int grp = wave % kGroups;
+  constexpr int kWgPerUnit = kUnitRows / (32 * kGroups);
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = unit_base + (logical >> 1);
+  const int unit = unit_base + logical / kWgPerUnit;
   const int head = unit / n_qtiles;
   const int qt = unit - head * n_qtiles;
-  const int row0 = qt * kUnitRows + (logical & 1) * 128;
+  const int row0 = qt * kUnitRows + (logical % kWgPerUnit) * (32 * kGroups);
   if (row0 >= Lq) return;   // the empty half of a ragged last unit (uniform per block)
   const size_t head_off = static_cast<size_t>(head) * Lq * D;
   const uint16_t *Kh = K + static_cast<size_t>(head) * kv_stride;
@@ -606,32 +609,40 @@ __global__ __launch_bounds__(512) void attn_tail_kernel(
   // Only the consumers (waves 4-7) load tiles: four 1-KB pieces each.
   auto dma = [&](const uint16_t *base, int t, const uint16_t *dst, bool is_k) {
     if (kVt && !is_k)
-      dma_vt_tile<4, true>(base, t, Lk, ldv, dst, wave - 4, wave_u - 4u, lane);
+      dma_vt_tile<kGroups, true>(base, t, Lk, ldv, dst, wave - kGroups, wave_u - kGroups, lane);
     else
-      dma_tile<4>(base, t, Lk, dst, is_k, wave - 4, wave_u - 4u, lane);
+      dma_tile<kGroups>(base, t, Lk, dst, is_k, wave - kGroups, wave_u - kGroups, lane);
   };
   auto end_step = [&]() {
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");   // all but this step's 8 loads
+    // All but this step's loads (16 / kGroups pieces per tensor and wave).
+    if constexpr (kGroups == 4)
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
   };
 
   const int n_kt = (Lk + kBc - 1) / kBc;
   const int n_steps = (n_kt + kSlots - 1) / kSlots * kSlots;   // as in attn_fwd_kernel
-  if (wave_u >= 4) {
+  if (wave_u >= kGroups) {
     dma(Kh, 0, k_lds[0], true);
     dma(Kh, 1, k_lds[1], true);
     dma(Kh, 2, k_lds[2], true);
     dma(Vh, 0, v_lds[0], false);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // K tiles 0 and 1
+    // K tiles 0 and 1 (K tile 2 and V tile 0 may still be in flight).
+    if constexpr (kGroups == 4)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   }
   __syncthreads();
 
-  if (wave_u < 4) {
+  if (wave_u < kGroups) {
     // Producer: scores, running max and weights of attn_fwd_kernel's step; P
     // and alpha to LDS.
     bf16x8 qf[8];
     {
-      const int rows_left = Lq - row0 < 128 ? Lq - row0 : 128;
+      const int rows_left = Lq - row0 < 32 * kGroups ? Lq - row0 : 32 * kGroups;
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_off + static_cast<size_t>(row0) * D, rows_left * (D * 2));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -815,11 +826,20 @@ hipError_t device_cu_count(int *cus) {
   return e;
 }
 
+// Groups of 32 rows per tail workgroup (a producer and a consumer wave
+// each).  Four groups put two waves on each SIMD; two give every wave a SIMD
+// of its own, which shortens a group's step but runs half the rows per CU.
+// Two pay only when the leftover units are few enough that the tail runs on
+// a small share of the CUs anyway (same-box A/B, bit-identical: L = 37726 at
+// H = 7, 12 leftover units, 4.913 against 4.985 ms; 51 or 128 leftover units
+// ran 8% and 60% slower with two).
+int tail_groups(int tail, int cus) { return tail * 16 <= cus ? 2 : 4; }
+
 // Main launch + tail launch.  Units run in rounds of one 8-wave workgroup per
 // CU; when the last round would leave at least half the CUs idle (r <= CUs/2
 // units left over), those r units instead run as 2r attn_tail_kernel
-// workgroups of 128 rows, one per CU, after the full rounds (the same stream
-// orders the two launches).  The tail round then keeps every SIMD busy with
+// workgroups of 128 rows (or 4r of 64 rows, see tail_groups), one per CU,
+// after the full rounds (the same stream orders the two launches).  The tail round then keeps every SIMD busy with
 // half a round's work.  Which launch a unit lands in depends on H and on the
 // device, but a row's arithmetic does not.
 template <bool kLse, bool kVt>
@@ -841,8 +861,12 @@ hipError_t launch_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (tail > 0) {
-    hipLaunchKernelGGL((attn_tail_kernel<kLse, kVt>), dim3(2 * tail), dim3(512), 0, stream, q, k, v, out, out32,
-                       lse, Lq, Lk, kv_stride, ldv, n_qtiles, main_units, sl2e);
+    if (tail_groups(tail, cus) == 2)
+      hipLaunchKernelGGL((attn_tail_kernel<kLse, kVt, 2>), dim3(4 * tail), dim3(256), 0, stream, q, k, v, out, out32,
+                         lse, Lq, Lk, kv_stride, ldv, n_qtiles, main_units, sl2e);
+    else
+      hipLaunchKernelGGL((attn_tail_kernel<kLse, kVt, 4>), dim3(2 * tail), dim3(512), 0, stream, q, k, v, out, out32,
+                         lse, Lq, Lk, kv_stride, ldv, n_qtiles, main_units, sl2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -140,7 +140,32 @@ def test_attention_tail_workgroups_bit_identical(gpu_lib, L):
         assert torch.equal(single[h], full[h]), f"head {h} differs between the launches"
 
 
-@pytest.mark.parametrize("H,L", [(1, 4096), (3, 1000)])
+def test_attention_tail_forms_bit_identical(gpu_lib):
+    """The three forms a row can run in: ten heads of 16 query tiles in one
+    launch (160 units, one partial round of the full-round kernel), one
+    launch per head (16 units: the tail launch with 64-row workgroups, one
+    wave per SIMD) and five launches of two heads (32 units: 128-row tail
+    workgroups).  Every head bit-identical, and the full launch within the
+    bars of the oracle on sampled rows."""
+    import torch
+    L = 4000
+    q, k, v = _raw(10, L, seed=4000)
+    w = I.custom_workload(H=10, L=L)
+    rows = [I.sample_rows(w, h, 256) for h in range(10)]
+    full = _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), rows, label=f"10 heads L={L}")
+    single = torch.empty_like(full)
+    for h in range(10):
+        gpu_lib.attention(q[h:h + 1], k[h:h + 1], v[h:h + 1], out=single[h:h + 1])
+    pairs = torch.empty_like(full)
+    for h in range(0, 10, 2):
+        gpu_lib.attention(q[h:h + 2], k[h:h + 2], v[h:h + 2], out=pairs[h:h + 2])
+    torch.cuda.synchronize()
+    for h in range(10):
+        assert torch.equal(single[h], full[h]), f"head {h}: one-head launch differs"
+        assert torch.equal(pairs[h], full[h]), f"head {h}: two-head launch differs"
+
+
+@pytest.mark.parametrize("H,L", [(1, 4096), (3, 1000), (1, 3000)])
 def test_attention_tail_launch_repeat_bit_identical(gpu_lib, H, L):
     """Race check of the tail launch's producer/consumer handoff through LDS:
     shapes whose units all run in the tail kernel, launched 20 times back to

@@ -86,13 +86,14 @@ def test_split_merge_equals_full(gpu_lib, cuts):
     check_attention_errors(f"cuts {cuts} merged", merge_errors(parts))
 
 
-def test_attention_lse_tail_workgroups_bit_identical(gpu_lib):
-    """The partial form through both kernels: ten heads in one launch (200
-    units: all in the main launch) against one launch per head (20 units: all
-    in the producer/consumer tail launch), over a key range given as a pointer
-    offset.  out and lse bit-identical per head."""
+@pytest.mark.parametrize("Lq", [4900, 4000])
+def test_attention_lse_tail_workgroups_bit_identical(gpu_lib, Lq):
+    """The partial form through both kernels: ten heads in one launch (200 or
+    160 units: all in the main launch) against one launch per head (20 units:
+    128-row tail workgroups; 16 units: 64-row tail workgroups), over a key
+    range given as a pointer offset.  out and lse bit-identical per head."""
     import torch
-    q, k, v = _raw(10, 4900, seed=44)
+    q, k, v = _raw(10, Lq, seed=44)
     a, b = 100, 4037
     out_all, lse_all = gpu_lib.attention_lse(q, k[:, a:b], v[:, a:b])
     for h in range(10):
