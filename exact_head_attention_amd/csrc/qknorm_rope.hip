@@ -7,7 +7,7 @@
 // the sum of squares crosses lanes (a 16-lane DPP reduction).
 //
 // A workgroup is 16 tokens of one head.  Workgroups are numbered by token
-// chunk of 32768, then by head, then by token, so the whole chip streams
+// chunk (of at most 32768), then by head, then by token, so the whole chip streams
 // through one head's share of q and k at a time: two long sequential streams,
 // which DRAM serves better (45.5 us cold at H = 7, L = 32768, 5.5 TB/s) than
 // every workgroup walking all H heads at once (50.4 us).  The cos/sin rows are
@@ -85,15 +85,23 @@ __device__ __forceinline__ uint4 norm_rope8(uint4 raw, const float g[8], const f
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Token chunks of kChunk: the grid walks chunk by chunk and, inside a chunk,
-// head by head.  A chunk's cos/sin rows (kChunk x 512 B, 2 MB per XCD at
-// 32768) stay in the XCDs' L2 while every head streams past them, and each
-// chunk's block count per head is a multiple of the 8 XCDs, so a token block
-// lands on the same XCD for every head.
-constexpr int kChunk = 32768;
+// Token chunks: the grid walks chunk by chunk and, inside a chunk, head by
+// head.  A chunk's cos/sin rows (up to 32768 x 512 B, 2 MB per XCD) stay in
+// the XCDs' L2 while every head streams past them, and each chunk's block
+// count per head is a multiple of the 8 XCDs, so a token block lands on the
+// same XCD for every head.  A sequence is cut into ceil(L / 32768) chunks of
+// equal size (rounded up to whole XCD rounds of blocks), so an odd length
+// such as 37726 makes two chunks of about 18900 tokens rather than 32768
+// plus a short tail.
+constexpr int kMaxChunk = 32768;
 constexpr int kXcds = 8;
-constexpr int kChunkBlocks = kChunk / kTokensPerBlock;
-static_assert(kChunkBlocks % kXcds == 0, "chunk blocks per head must be a multiple of the XCD count");
+constexpr int kChunkQuantum = kTokensPerBlock * kXcds;   // tokens per XCD round of blocks
+
+__host__ __device__ inline int chunk_tokens(int L) {
+  const int n = (L + kMaxChunk - 1) / kMaxChunk;
+  const int c = (L + n - 1) / n;
+  return (c + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+}
 
 // Blocks per head for the last, partial chunk of rem tokens.
 __host__ __device__ inline int tail_chunk_blocks(int rem) {
@@ -104,23 +112,25 @@ __global__ __launch_bounds__(kTokensPerBlock * 16) void qknorm_rope_kernel(
     uint16_t *__restrict__ q, uint16_t *__restrict__ k, const float *__restrict__ gamma_q,
     const float *__restrict__ gamma_k, const float *__restrict__ cos_t,
     const float *__restrict__ sin_t, int H, int L, float eps) {
-  const int full = L / kChunk;
-  const int full_blocks = full * H * kChunkBlocks;
+  const int chunk_len = chunk_tokens(L);
+  const int chunk_blocks = chunk_len / kTokensPerBlock;
+  const int full = L / chunk_len;
+  const int full_blocks = full * H * chunk_blocks;
   int b = blockIdx.x, chunk, head, tb;
   if (b < full_blocks) {
-    chunk = b / (H * kChunkBlocks);
-    b -= chunk * H * kChunkBlocks;
-    head = b / kChunkBlocks;
-    tb = b - head * kChunkBlocks;
+    chunk = b / (H * chunk_blocks);
+    b -= chunk * H * chunk_blocks;
+    head = b / chunk_blocks;
+    tb = b - head * chunk_blocks;
   } else {
-    const int per_head = tail_chunk_blocks(L - full * kChunk);
+    const int per_head = tail_chunk_blocks(L - full * chunk_len);
     b -= full_blocks;
     chunk = full;
     head = b / per_head;
     tb = b - head * per_head;
   }
   const int sub = threadIdx.x & 15;                       // lane within the 16-lane row
-  const int tok = chunk * kChunk + tb * kTokensPerBlock + (threadIdx.x >> 4);
+  const int tok = chunk * chunk_len + tb * kTokensPerBlock + (threadIdx.x >> 4);
   if (tok >= L) return;                                   // whole 16-lane rows exit together
 
   const size_t off = (static_cast<size_t>(head) * L + tok) * kHeadDim + 8 * sub;
@@ -164,9 +174,11 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(const int *__restrict_
 hipError_t launch_qknorm_rope(uint16_t *q, uint16_t *k, const float *gamma_q, const float *gamma_k,
                               const float *cos_t, const float *sin_t, int H, int L, float eps,
                               hipStream_t stream) {
-  const int full = L / kChunk, rem = L - full * kChunk;
-  // < 2^31: H*L < 2^31 is validated, and padding adds under 8 blocks per head
-  const int64_t blocks = static_cast<int64_t>(H) * (static_cast<int64_t>(full) * kChunkBlocks +
+  const int chunk_len = chunk_tokens(L);
+  const int full = L / chunk_len, rem = L - full * chunk_len;
+  // < 2^31: H*L < 2^31 is validated, and padding adds under 8 blocks per
+  // head and chunk
+  const int64_t blocks = static_cast<int64_t>(H) * (static_cast<int64_t>(full) * (chunk_len / kTokensPerBlock) +
                                                     (rem > 0 ? tail_chunk_blocks(rem) : 0));
   hipLaunchKernelGGL(qknorm_rope_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kTokensPerBlock * 16), 0, stream,
                      q, k, gamma_q, gamma_k, cos_t, sin_t, H, L, eps);
