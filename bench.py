@@ -7,7 +7,8 @@ Default workload: one world_size=8 rank's share, H=7 heads, L=32768 tokens
 
 Prints one JSON line: whole-step attention TFLOPS (4*H*L^2*D per step), the
 roofline of the dominant kernel (attention, bf16 MFMA) from HIP events around
-its launches, the prologue's bandwidth, the same attention and prologue
+its launches, the prologue's bandwidth (beside a plain device copy of the same
+bytes, timed the same way), the same attention and prologue
 figures for the other rank shares (H=28, H=56, and the odd length 37726) timed
 in the same run, and the oracle's CPU throughput on the workload's sampled
 rows (reported baseline only).
@@ -626,6 +627,7 @@ def main():
     log(f"bench: {w.name} step {ms_step:.3f} ms, attention {att_ms:.3f} ms")
 
     pro_cold_ms = prologue_cold_ms(B, q, k, gq, gk, cos, sin, x["eps"])
+    pro_copy_ms = copy_cold_ms(prologue_bytes(w.H, w.L, w.D), dev)
 
     # Back to back, the way the prologue runs inside a pipeline: launches with
     # no event or flush between them, on six distinct q/k sets (6 x 117 MB,
@@ -694,7 +696,8 @@ def main():
                      "frac": round(att_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(att_ms, 4), "min_launch_ms": round(min(att_ms_all), 4),
                      "flops_per_launch": flops},
-        "prologue": prologue_record(pbytes, pro_ms, pro_cold_ms, pro_b2b_ms, read_prologue_traffic(w.name)),
+        "prologue": prologue_record(pbytes, pro_ms, pro_cold_ms, pro_b2b_ms, read_prologue_traffic(w.name),
+                                    copy_ms=pro_copy_ms),
     }
     counters = read_sq_summary(w.name)
     if counters is not None or traffic is not None:
@@ -766,12 +769,39 @@ def prologue_cold_ms(B, q, k, gq, gk, cos, sin, eps, reps=20):
     return float(np.median(cold))
 
 
-def prologue_record(pbytes, pro_ms, cold_ms, b2b_ms=None, traffic=None):
+def copy_cold_ms(nbytes, device, reps=20):
+    """Median time of a plain device-to-device copy (torch's copy_) that reads
+    nbytes / 2 and writes nbytes / 2, timed like prologue_cold_ms: the
+    streaming rate this machine reaches for the prologue's mix of reads and
+    writes, beside the published HBM peak."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=device)
+    src = torch.ones(nbytes // 2, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    times = []
+    for _ in range(reps):
+        flush.amax()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush, src, dst
+    return float(np.median(times))
+
+
+def prologue_record(pbytes, pro_ms, cold_ms, b2b_ms=None, traffic=None, copy_ms=None):
     rec = {"kernel": "qknorm_rope_kernel", "bound": "hbm", "bytes_per_launch": pbytes, "peak_GBps": HBM_PEAK_GBS,
            "avg_launch_us_in_step": round(pro_ms * 1e3, 2),
            "cold_median_us": round(cold_ms * 1e3, 2),
            "achieved_GBps_cold": round(pbytes / (cold_ms / 1e3) / 1e9, 1),
            "frac_cold": round(pbytes / (cold_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if copy_ms is not None:
+        rec.update(copy_cold_us=round(copy_ms * 1e3, 2),
+                   copy_GBps_cold=round(pbytes / (copy_ms / 1e3) / 1e9, 1),
+                   cold_vs_copy=round(copy_ms / cold_ms, 4))
     if b2b_ms is not None:
         rec.update(back_to_back_us=round(b2b_ms * 1e3, 2),
                    achieved_GBps_back_to_back=round(pbytes / (b2b_ms / 1e3) / 1e9, 1),
@@ -798,6 +828,7 @@ def bench_extra_workload(name, args, steps=10, warmup=2):
     out = torch.empty_like(q)
     pro_ms = float(np.mean(time_calls(lambda: B.qknorm_rope(q, k, gq, gk, cos, sin, I.RMS_EPS), 1, 5)))
     cold_ms = prologue_cold_ms(B, q, k, gq, gk, cos, sin, I.RMS_EPS, reps=10)
+    copy_ms = copy_cold_ms(prologue_bytes(w.H, w.L, w.D), q.device, reps=10)
     att = time_calls(lambda: B.attention(q, k, v, out=out, scale=w.attn_scale), warmup, steps)
     att_ms = float(np.mean(att))
     tf = w.flops / (att_ms / 1e3) / 1e12
@@ -807,7 +838,7 @@ def bench_extra_workload(name, args, steps=10, warmup=2):
     return {"H": w.H, "L": w.L, "attention": {"avg_launch_ms": round(att_ms, 4), "min_launch_ms": round(min(att), 4),
                                               "achieved": round(tf, 2), "unit": "TFLOP/s",
                                               "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "calls": steps},
-            "prologue": prologue_record(prologue_bytes(w.H, w.L, w.D), pro_ms, cold_ms)}
+            "prologue": prologue_record(prologue_bytes(w.H, w.L, w.D), pro_ms, cold_ms, copy_ms=copy_ms)}
 
 
 if __name__ == "__main__":
