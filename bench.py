@@ -130,12 +130,16 @@ def summarize(args):
         out.append(f"# command: {args.command}")
         src = args.source or ATTN_SOURCE
         out.append(f"# {os.path.basename(src)} sha256[:16] = {source_digest(src)}")
-        out.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
-        call_us = 0.0
+        out.append(f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'med_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+                   f"{'pct':>6s}")
+        med = _trace_medians(args.kernel_stats)
+        call_us, call_med_us = 0.0, 0.0
         for r in rows:
             name = _kernel_short(r["Name"])
-            if name in ("attn_fwd_kernel<false, false>", "attn_tail_kernel<false, false>"):
+            # The tail kernel's name carries its group count: <false, false, 2> or <false, false, 4>.
+            if name == "attn_fwd_kernel<false, false>" or name.startswith("attn_tail_kernel<false, false,"):
                 call_us += float(r["AverageNs"]) / 1e3
+                call_med_us += med.get(r["Name"], float("nan"))
             if "reduce_kernel" in r["Name"]:
                 name = "torch amax (read-only cache flush)"
             elif "FillFunctor" in r["Name"] or "fillBuffer" in r["Name"]:
@@ -144,10 +148,12 @@ def summarize(args):
                 name = ("device copies (largest = 512 MiB calibration)" if float(r["MaxNs"]) > 1e5
                         else "device copies (small uploads)")
             out.append(f"{name[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                       f"{med.get(r['Name'], float('nan')):10.2f} "
                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
         if call_us > 0:
             out.append(f"# one h3_attention call = attn_fwd_kernel<false, false> (full rounds) + "
-                       f"attn_tail_kernel<false, false> (tail, when launched): {call_us:.2f} us per call")
+                       f"attn_tail_kernel<false, false, groups> (tail, when launched): {call_us:.2f} us per call "
+                       f"on average over every dispatch (warmup included), {call_med_us:.2f} us from the medians")
         out += _prologue_split(args.kernel_stats)
     if args.pmc:
         per = {}
@@ -155,7 +161,7 @@ def summarize(args):
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
                     key = ("attn_main" if "attn_fwd_kernel<false, false>" in r["Kernel_Name"] else
-                           "attn_tail" if "attn_tail_kernel<false, false>" in r["Kernel_Name"] else
+                           "attn_tail" if "attn_tail_kernel<false, false," in r["Kernel_Name"] else
                            "prologue" if "qknorm_rope_kernel" in r["Kernel_Name"] else
                            "copy" if "copyBuffer" in r["Kernel_Name"] else None)
                     if key:
@@ -180,6 +186,15 @@ def summarize(args):
     if args.sq:
         out += _sq_summary(args)
     print("\n".join(out))
+
+
+def _trace_medians(trace_dir):
+    """Median duration (us) per kernel name over the dispatches of a kernel trace."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    per = {}
+    for r in (csv.DictReader(open(files[0])) if files else []):
+        per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: float(np.median(v)) for k, v in per.items()}
 
 
 def _prologue_split(trace_dir):
@@ -221,7 +236,7 @@ def _sq_summary(args):
         fp8 = args.workload.startswith("proj8")
         kernels = (("main", f"qkv_proj_kernel<{'true' if fp8 else 'false'}>"),)
     else:
-        kernels = (("main", "attn_fwd_kernel<false, false>"), ("tail", "attn_tail_kernel<false, false>"))
+        kernels = (("main", "attn_fwd_kernel<false, false>"), ("tail", "attn_tail_kernel<false, false,"))
     src = args.source or ATTN_SOURCE
     vals, clocks = {}, []
     for d in args.sq:
@@ -234,7 +249,7 @@ def _sq_summary(args):
                             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
                             clocks.append(float(r["Counter_Value"]) / SHADER_ENGINES / dur / 1e9)
     out = [f"# rocprofv3 --pmc, {len(args.sq)} passes of SQ counters, workload {args.workload}: "
-           + " and ".join(f"{k} ({key})" for key, k in kernels),
+           + " and ".join(f"{k + ' groups>' if k.endswith(',') else k} ({key})" for key, k in kernels),
            f"# commands: {args.command}",
            f"# {os.path.basename(src)} sha256[:16] = {source_digest(src)}",
            f"# mean per dispatch (sums over the chip); {SHADER_ENGINES} shader engines, {SIMDS} SIMDs; "
