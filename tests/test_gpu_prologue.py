@@ -114,3 +114,36 @@ def test_prologue_ragged_lengths(gpu_lib, L):
     that ends 45 tokens into a second 32768-token chunk."""
     w = I.custom_workload(H=3, L=L, n_audio=L // 3)
     _prologue_check(gpu_lib, I.make_inputs(w, seed=L), f"L={L}")
+
+
+def test_prologue_one_norm_per_token(gpu_lib):
+    """All 16 lanes of a token must normalise by the same r.  With gamma = 1,
+    cos = 1 and sin = 0 an output element is RNE(fl(x * r)), so when one lane
+    holds exactly twice another lane's values (a power of two commutes with
+    both roundings) its outputs must be exactly twice the other's.  Elements
+    32..63 (lanes 4-7) are set to 2x elements 0..31 (lanes 0-3), and 96..127
+    to 2x 64..95: partners in different quads of the 16-lane row, where a
+    reduction that summed in a different order per quad would give r values
+    one fp32 ulp apart on some tokens.  A build with such a reduction (quad
+    sums combined by row rotations) failed this check on 17 elements of q
+    and 24 of k; the butterfly passes with none."""
+    import torch
+    H, L = 7, 32768
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    xs = []
+    for _ in range(2):
+        x = torch.randn((H, L, 128), generator=g, device="cuda:0").to(torch.bfloat16)
+        x[:, :, 32:64] = x[:, :, 0:32] * 2
+        x[:, :, 96:128] = x[:, :, 64:96] * 2
+        xs.append(x)
+    q, k = xs
+    ones = torch.ones(128, dtype=torch.float32, device="cuda:0")
+    cos = torch.ones((L, 64), dtype=torch.float32, device="cuda:0")
+    sin = torch.zeros((L, 64), dtype=torch.float32, device="cuda:0")
+    gpu_lib.qknorm_rope(q, k, ones, ones, cos, sin, 1e-6)
+    torch.cuda.synchronize()
+    for name, t in (("q", q), ("k", k)):
+        f = t.float()
+        bad = int((f[:, :, 32:64] != 2 * f[:, :, 0:32]).sum()) + int((f[:, :, 96:128] != 2 * f[:, :, 64:96]).sum())
+        print(f"{name}: {bad} elements not exactly twice their partner")
+        assert bad == 0
