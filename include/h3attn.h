@@ -69,6 +69,9 @@ typedef enum {
  * the tables broadcast over heads (see the passages above).
  *
  *   q, k          bf16 [H][L][D], read and overwritten.  Must not overlap.
+ *                 Finite values whose sum of squares per token stays finite
+ *                 in fp32 (every |x_d| below about 2^63); larger rows are
+ *                 out of contract.
  *   gamma_q/_k    fp32 [D], shared by all heads.
  *   cos, sin      fp32 [L][D/2]: entry (i, j) is cos/sin of token i's rotary
  *                 angle for pair j (h3_rope_tables builds them).
