@@ -189,6 +189,44 @@ def test_attention_peaky_logits(gpu_lib):
     _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), label="peaky")
 
 
+def test_attention_hard_max(gpu_lib):
+    """q, k ~ 100 N(0,1): logits with a standard deviation near 10^4, so the
+    running max rises through many orders of magnitude (rescale factors that
+    flush to exactly 0) and about 93% of rows have a runner-up more than 200
+    below the top logit, i.e. weights one-hot far below bf16 resolution.
+    Each such row must be the V row of its largest score, bit for bit, as
+    the oracle's rounded result is; every row meets the usual bars.  Both
+    launch forms: 10 heads of L = 4900 (main launch) and 3 heads of 1000
+    (tail)."""
+    import torch
+    for H, L in ((10, 4900), (3, 1000)):
+        q, k, v = _raw(H, L, seed=11 + L, mult=100.0)
+        out = gpu_lib.attention(q, k, v)
+        torch.cuda.synchronize()
+        qb, kb, vb, ob = bits(q), bits(k), bits(v), bits(out)
+        for h in range(H):
+            s = oracle.bf16_to_f64(qb[h]) @ oracle.bf16_to_f64(kb[h]).T
+            top = np.sort(s, axis=1)[:, -2:]
+            gap = (top[:, 1] - top[:, 0]) / math.sqrt(128)
+            one_hot = gap > 200.0          # the runner-up weighs below e^-200
+            assert one_hot.mean() > 0.85
+            want = vb[h][np.argmax(s, axis=1)]
+            assert np.array_equal(ob[h][one_hot], want[one_hot]), f"H={H} L={L} head {h}"
+        _attention_vs_oracle(gpu_lib, q, k, v, 1 / math.sqrt(128), label=f"hard max H={H} L={L}", out=out)
+
+
+def test_attention_zero_queries_and_keys(gpu_lib):
+    """All-zero query rows or all-zero keys give every key the same weight:
+    the output is the mean of V (the oracle's value, on the usual bars)."""
+    import torch
+    H, L = 2, 1500
+    q, k, v = _raw(H, L, seed=21)
+    q0 = q.clone()
+    q0[:, ::3] = 0                         # every third query row zero
+    _attention_vs_oracle(gpu_lib, q0, k, v, 1 / math.sqrt(128), label="zero query rows")
+    _attention_vs_oracle(gpu_lib, q, torch.zeros_like(k), v, 1 / math.sqrt(128), label="zero keys")
+
+
 def _sampled_workload(gpu_lib, name, with_prologue=True):
     x = host_inputs(name)
     w = I.WORKLOADS[name]

@@ -77,7 +77,10 @@ def _prologue_check(gpu_lib, x, label):
         err = np.abs(g64 - y)
         ulps = bf16_ulp_distance(got, yb)
         frac = float(np.mean(got != yb))
-        rel = row_rel_err(got.reshape(-1, 128), y.reshape(-1, 128))
+        # Rows whose exact value is zero have no relative error; the element
+        # check above covers them.
+        nz = np.linalg.norm(y.reshape(-1, 128), axis=-1) > 0
+        rel = row_rel_err(got.reshape(-1, 128)[nz], y.reshape(-1, 128)[nz])
         print(f"{label} {nm}: max ulp vs RNE(ref) {ulps.max():.0f} (elements > 1 ulp: {int((ulps > 1).sum())}), "
               f"mismatching {frac:.2e}, max err/slack {float((err / slack).max()):.3f}, max row rel {rel.max():.2e}")
         assert np.all(err <= slack)
@@ -147,3 +150,23 @@ def test_prologue_one_norm_per_token(gpu_lib):
         bad = int((f[:, :, 32:64] != 2 * f[:, :, 0:32]).sum()) + int((f[:, :, 96:128] != 2 * f[:, :, 64:96]).sum())
         print(f"{name}: {bad} elements not exactly twice their partner")
         assert bad == 0
+
+
+def test_prologue_zero_tokens(gpu_lib):
+    """Tokens whose q or k row is all zero: r = 1/sqrt(eps) multiplies
+    zeros, so the row stays exactly zero (+0 or -0: the rotation's products
+    with a negative cos or sin carry the sign); the other tokens are
+    unaffected (checked against the oracle as usual)."""
+    import torch
+    w = I.custom_workload(H=3, L=1000, n_audio=200)
+    x = dict(I.make_inputs(w, seed=23))
+    for n in ("q", "k"):
+        a = x[n].copy()
+        a[:, ::7] = 0
+        x[n] = a
+    _prologue_check(gpu_lib, x, "zero tokens")
+    d = device_inputs(x)
+    cos, sin = gpu_lib.rope_tables(d["positions"], 128, x["theta"])
+    gpu_lib.qknorm_rope(d["q"], d["k"], d["gamma_q"], d["gamma_k"], cos, sin, x["eps"])
+    torch.cuda.synchronize()
+    assert np.all(bits(d["q"])[:, ::7] & 0x7FFF == 0) and np.all(bits(d["k"])[:, ::7] & 0x7FFF == 0)
