@@ -8,8 +8,9 @@
 // Work decomposition
 //   * Work unit = one (head, 256-query tile); each wave owns 32 query rows.
 //     A unit runs as one 8-wave workgroup, or, in the tail launch, as two
-//     8-wave workgroups of 128 rows each in which two waves share each 32-row
-//     group (attn_tail_kernel; see launch_split below).
+//     8-wave workgroups of 128 rows (or, when only a few units are left
+//     over, four 4-wave workgroups of 64 rows) in which two waves share each
+//     32-row group (attn_tail_kernel; see launch_split below).
 //   * Keys stream in tiles of 64 through a 4-slot LDS ring per tensor, K and
 //     V both row-major [key][d] with an XOR swizzle of the 16-byte chunks.
 //     Tiles move from global memory straight into LDS (buffer loads with the
